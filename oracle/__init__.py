@@ -1,0 +1,25 @@
+"""CPU fp64 oracle for block-diagonal causal attention over packed users.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg use it.  It shares no code with the HIP
+library in ``varlen_causal_attention_amd`` and imports nothing from it.
+
+Contents:
+  attention.varlen_causal_attention   per-user dense softmax(scale*QK^T + causal mask) V
+  attention.dense_masked_attention    whole packed stream as one T x T problem with the
+                                      block-diagonal causal mask built from the offsets
+  attention.block_diagonal_causal_mask
+  worklist.reference_worklist         the segment scheduler's (user, q-tile) order
+
+Every function is pinned by ``tests/test_oracle.py`` to something other than
+itself (brute force, closed forms, invariants, a library routine on the
+single-segment special case, hand-derived fixtures under ``tests/golden/``).
+"""
+from .attention import (  # noqa: F401
+    block_diagonal_causal_mask,
+    dense_masked_attention,
+    split_qkv_head,
+    varlen_causal_attention,
+)
+from .worklist import reference_worklist, tiles_per_user  # noqa: F401
