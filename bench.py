@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the varlen causal attention forward on one MI355X.
+
+One step = one call of varlen_causal_attn_fwd (segment scheduler + attention
+kernel) over the packed batch, with qkv and cu_seqlens already resident in HBM.
+Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+The default workload is the pages' size: 6823 packed tokens over 60 users,
+8 heads x 64, bf16 qkv [6823, 1536] (synthetic, seeded; see workloads.py).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+KERNEL_SRC = os.path.join(ROOT, "varlen_causal_attention_amd", "csrc", "vlca_kernels.hip")
+ATTN_KERNEL = "attention_kernel"
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attention_kernel_{workload_name}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle as it stands, timed on this host over whole passes of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    q = w.qkv_bf16.to(torch.float64).numpy()
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.varlen_causal_attention(q, w.cu_seqlens, w.n_heads, w.head_dim, w.scale)
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": passes * w.total_tokens / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{passes} full pass(es) of the {w.name} batch ({w.total_tokens} tokens, {w.num_users} users), "
+                  f"fp64 numpy, {dt:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = 6823 tokens / 60 users)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(users shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import varlen_causal_attention_amd as vlca
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = workloads.make_config(args.config)
+    qkv = w.qkv_bf16.to(dev)
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    out = torch.empty((w.total_tokens, w.n_heads * w.head_dim), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        vlca.fwd(qkv, cu, w.max_seqlen, n_heads=w.n_heads, head_dim=w.head_dim, scale=w.scale, out=out)
+
+    print(f"[bench] {w.name}: T={w.total_tokens} U={w.num_users} max_seqlen={w.max_seqlen} "
+          f"warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Whole hot path: K steps back to back between two events on the launch stream.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # Dominant kernel alone: the attention kernel over a prebuilt worklist, launched
+    # back to back on the same stream, timed with events on that stream.
+    items, _count = vlca.build_worklist(cu, w.max_seqlen)
+    for _ in range(args.warmup):
+        vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, scale=w.scale, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] step {ms_step * 1e3:.2f} us, attention kernel {ms_attn * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
+
+    flops = w.causal_flops()
+    nbytes = w.algorithmic_bytes()
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    ai = flops / nbytes
+    if ai < RIDGE:
+        bound, achieved, peak, unit = "hbm", nbytes / (ms_attn * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / (ms_attn * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    traffic = measured_traffic(w.name)
+
+    rec = {
+        "metric": "varlen causal attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), 6823tok/60users",
+        "value": w.total_tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "total_tokens": w.total_tokens,
+            "num_users": w.num_users,
+            "max_seqlen": w.max_seqlen,
+            "n_heads": w.n_heads,
+            "head_dim": w.head_dim,
+            "qkv": f"bf16 [{w.total_tokens}, {3 * w.n_heads * w.head_dim}]",
+            "length_law": "lognormal(4.3, 0.9) rescaled, seed 0" if args.config == 2 else "see workloads.py",
+        },
+        "tflops": tflops,
+        "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "causal_gflop": flops / 1e9,
+        "roofline": {
+            "bound": bound,
+            "achieved": achieved,
+            "peak": peak,
+            "unit": unit,
+            "frac": achieved / peak,
+            "traffic": traffic,
+            "kernel": ATTN_KERNEL,
+            "kernel_us": ms_attn * 1e3,
+            "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

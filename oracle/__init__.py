@@ -7,6 +7,7 @@ library in ``varlen_causal_attention_amd`` and imports nothing from it.
 
 Contents:
   attention.varlen_causal_attention   per-user dense softmax(scale*QK^T + causal mask) V
+  attention.varlen_causal_attention_rows  the same, one selected query row at a time
   attention.dense_masked_attention    whole packed stream as one T x T problem with the
                                       block-diagonal causal mask built from the offsets
   attention.block_diagonal_causal_mask
@@ -21,5 +22,6 @@ from .attention import (  # noqa: F401
     dense_masked_attention,
     split_qkv_head,
     varlen_causal_attention,
+    varlen_causal_attention_rows,
 )
 from .worklist import reference_worklist, tiles_per_user  # noqa: F401

@@ -70,6 +70,33 @@ def varlen_causal_attention(qkv: np.ndarray, cu_seqlens, n_heads: int, head_dim:
     return out
 
 
+def varlen_causal_attention_rows(qkv: np.ndarray, cu_seqlens, rows, n_heads: int, head_dim: int,
+                                 scale: float) -> np.ndarray:
+    """fp64 output of the selected packed rows only, ``[len(rows), n_heads*head_dim]``.
+
+    Row ``r`` of user ``u`` (``cu[u] <= r < cu[u+1]``) attends to rows ``cu[u] .. r``:
+    the same definition as ``varlen_causal_attention`` evaluated one query at a
+    time, so full-size batches can be checked on a sample of rows.
+    """
+    qkv = np.asarray(qkv)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    hd = n_heads * head_dim
+    out = np.zeros((len(rows), hd), dtype=np.float64)
+    for n, r in enumerate(rows):
+        u = int(np.searchsorted(cu, r, side="right")) - 1
+        s = int(cu[u])
+        keys = slice(s, int(r) + 1)
+        for h in range(n_heads):
+            c = h * head_dim
+            q = np.asarray(qkv[r, c:c + head_dim], dtype=np.float64)
+            k = np.asarray(qkv[keys, hd + c:hd + c + head_dim], dtype=np.float64)
+            v = np.asarray(qkv[keys, 2 * hd + c:2 * hd + c + head_dim], dtype=np.float64)
+            z = scale * (k @ q)
+            e = np.exp(z - z.max())
+            out[n, c:c + head_dim] = (e / e.sum()) @ v
+    return out
+
+
 def block_diagonal_causal_mask(cu_seqlens) -> np.ndarray:
     """Dense boolean ``[T, T]`` mask: entry (i, j) is True iff rows i and j belong to
     the same user and j <= i.

@@ -1,0 +1,112 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments on the
+host before any device work (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import varlen_causal_attention_amd as vlca
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "varlen_causal_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s+(varlen_causal_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(vlca.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = vlca.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", vlca.library_path()], capture_output=True, text=True)
+    if nm.returncode == 0:
+        exported = set(ln.split()[-1] for ln in nm.stdout.splitlines() if ln.strip())
+        for name in declared_functions():
+            assert name in exported, name
+
+
+def test_header_compiles_as_c():
+    src = f'#include "{HEADER}"\nint main(void) {{ return varlen_causal_attn_tile_rows() == 64 ? 0 : 1; }}\n'
+    res = subprocess.run(["gcc", "-std=c11", "-fsyntax-only", "-x", "c", "-"], input=src, capture_output=True,
+                         text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_constants_and_strings():
+    assert vlca.tile_rows() == 64
+    assert vlca.strerror(0) == "success"
+    for code in range(-10, 0):
+        assert vlca.strerror(code) != "unknown error code"
+    assert vlca.strerror(-99) == "unknown error code"
+
+
+def test_worklist_capacity():
+    assert vlca.worklist_capacity(60, 452) == 60 * 8 + 4096
+    assert vlca.worklist_capacity(0, 0) == 4096
+    assert vlca.worklist_capacity(1000, 4096) == 1000 * 64 + 4096
+    with pytest.raises(vlca.VlcaError) as e:
+        vlca.worklist_capacity(-1, 10)
+    assert e.value.code == -2
+    with pytest.raises(vlca.VlcaError) as e:
+        vlca.worklist_capacity(10, 262145)
+    assert e.value.code == -6
+    with pytest.raises(vlca.VlcaError) as e:
+        vlca.worklist_capacity(600000, 262144)  # > 2^31 items
+    assert e.value.code == -6
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _fwd(qkv=FAKE, cu=FAKE, U=4, ms=40, H=8, D=64, scale=0.125, out=FAKE * 2):
+    return vlca.library().varlen_causal_attn_fwd(qkv, cu, U, ms, H, D, ctypes.c_float(scale), out, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(U=-1), -2),
+    (dict(ms=-5), -2),
+    (dict(D=128), -3),
+    (dict(D=32), -3),
+    (dict(H=0), -4),
+    (dict(H=70000), -4),
+    (dict(scale=float("nan")), -5),
+    (dict(scale=float("inf")), -5),
+    (dict(scale=0.0), -5),
+    (dict(scale=-0.125), -5),
+    (dict(ms=262145), -6),
+    (dict(qkv=None), -1),
+    (dict(cu=None), -1),
+    (dict(out=None), -1),
+    (dict(out=FAKE), -8),
+])
+def test_fwd_rejects_bad_arguments_before_device_work(kwargs, code):
+    assert _fwd(**kwargs) == code
+
+
+def test_fwd_zero_users_or_zero_length_is_a_noop():
+    # No device is touched: these return before any HIP call.
+    assert _fwd(qkv=None, cu=None, out=None, U=0) == 0
+    assert _fwd(ms=0) == 0
+
+
+def test_build_worklist_and_fwd_worklist_validation():
+    lib = vlca.library()
+    assert lib.varlen_causal_attn_build_worklist(FAKE, 4, 40, None, 5000, FAKE, None) == -1
+    assert lib.varlen_causal_attn_build_worklist(FAKE, 4, 40, FAKE, 5000, None, None) == -1
+    assert lib.varlen_causal_attn_build_worklist(None, 4, 40, FAKE, 5000, FAKE, None) == -1
+    assert lib.varlen_causal_attn_build_worklist(FAKE, 4, 40, FAKE, 4099, FAKE, None) == -7
+    assert lib.varlen_causal_attn_build_worklist(FAKE, -4, 40, FAKE, 9999, FAKE, None) == -2
+    f = lib.varlen_causal_attn_fwd_worklist
+    c = ctypes.c_float(0.125)
+    assert f(FAKE, FAKE, 4, 40, 8, 64, c, None, 5000, FAKE * 2, None) == -1
+    assert f(FAKE, FAKE, 4, 40, 8, 64, c, FAKE, 4099, FAKE * 2, None) == -7
+    assert f(FAKE, FAKE, 4, 40, 8, 96, c, FAKE, 5000, FAKE * 2, None) == -3
+    assert f(None, None, 0, 40, 8, 64, c, None, 0, None, None) == 0

@@ -1,0 +1,139 @@
+"""Properties of the HIP path that must hold exactly (GPU): run-to-run identity,
+isolation across users, invariance to max_seqlen, to zero-length users and to
+user order, exact length-one rows, plus closed-form cases within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import varlen_causal_attention_amd as vlca
+import workloads
+from gpu_util import TOL_MAX, assert_close, qkv64, run_fwd, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def user_rows(cu, u):
+    return slice(int(cu[u]), int(cu[u + 1]))
+
+
+@pytest.mark.parametrize("idx", [2, 5])
+def test_run_twice_bit_identical(gpu, idx):
+    w = workloads.make_config(idx)
+    say(f"[case] run twice, config {idx}")
+    qkv, cu = to_gpu(w)
+    a = run_fwd(w, qkv=qkv, cu=cu)
+    b = run_fwd(w, qkv=qkv, cu=cu)
+    assert torch.equal(a, b)
+
+
+def test_isolation_other_users_bit_identical(gpu):
+    w = workloads.make_config(2)
+    say("[case] isolation, config 2 user 7")
+    base = run_fwd(w)
+    pert = workloads.make_config(2)
+    r = user_rows(w.cu_seqlens, 7)
+    pert.qkv_bf16[r] = (pert.qkv_bf16[r].float() * -1.5 + 0.25).to(torch.bfloat16)
+    out = run_fwd(pert)
+    keep = torch.ones(w.total_tokens, dtype=torch.bool)
+    keep[r] = False
+    assert torch.equal(base[keep], out[keep])
+    assert not torch.equal(base[~keep], out[~keep])
+
+
+def test_max_seqlen_invariance(gpu):
+    w = workloads.make_config(2)
+    say("[case] max_seqlen 452 / 1024 / 2048 / 262144")
+    qkv, cu = to_gpu(w)
+    ref = run_fwd(w, qkv=qkv, cu=cu)
+    for ms in (1024, 2048, 262144):
+        assert torch.equal(ref, run_fwd(w, max_seqlen=ms, qkv=qkv, cu=cu)), ms
+
+
+def test_zero_length_users_change_nothing(gpu):
+    w = workloads.make_config(2)
+    say("[case] zero-length users inserted")
+    base = run_fwd(w)
+    L = list(w.lengths)
+    L2 = [0, 0] + L[:10] + [0] + L[10:30] + [0, 0, 0] + L[30:] + [0]
+    w2 = workloads.Workload("padded", np.asarray(L2), workloads.cu_from_lengths(L2), w.max_seqlen, w.scale)
+    w2.qkv_bf16 = w.qkv_bf16
+    assert torch.equal(base, run_fwd(w2))
+
+
+def test_user_order_permutation(gpu):
+    w = workloads.make_config(3)
+    say("[case] user permutation, config 3")
+    base = run_fwd(w)
+    perm = np.random.default_rng(5).permutation(w.num_users)
+    rows = np.concatenate([np.arange(w.cu_seqlens[u], w.cu_seqlens[u + 1]) for u in perm])
+    L2 = w.lengths[perm]
+    w2 = workloads.Workload("perm", L2, workloads.cu_from_lengths(L2), w.max_seqlen, w.scale)
+    w2.qkv_bf16 = w.qkv_bf16[torch.from_numpy(rows)]
+    out = run_fwd(w2)
+    assert torch.equal(out, base[torch.from_numpy(rows)])
+
+
+def test_length_one_rows_exact(gpu):
+    w = workloads.make_from_lengths([1, 5, 1, 1, 300, 1], seed=2)
+    say("[case] length-one users")
+    out = run_fwd(w)
+    for u, L in enumerate(w.lengths):
+        if L == 1:
+            r = int(w.cu_seqlens[u])
+            assert torch.equal(out[r], w.qkv_bf16[r, 1024:])
+
+
+def test_zero_query_gives_running_mean(gpu):
+    w = workloads.make_from_lengths([5, 90, 200, 1], seed=3)
+    w.qkv_bf16[:, :512] = 0
+    say("[case] q = 0")
+    out = run_fwd(w).double().numpy()
+    v = qkv64(w)[:, 1024:]
+    for u in range(w.num_users):
+        s, e = int(w.cu_seqlens[u]), int(w.cu_seqlens[u + 1])
+        want = np.cumsum(v[s:e], axis=0) / np.arange(1, e - s + 1)[:, None]
+        assert np.max(np.abs(out[s:e] - want)) <= TOL_MAX
+
+
+def test_constant_v(gpu):
+    w = workloads.make_from_lengths([7, 150, 64], seed=4)
+    c = torch.linspace(-3, 3, 512).to(torch.bfloat16)
+    w.qkv_bf16[:, 1024:] = c
+    say("[case] constant v")
+    out = run_fwd(w)
+    # weights are renormalised by the sum of the rounded weights: exact up to fp32 accumulation
+    assert torch.max(torch.abs(out.float() - c.float()[None, :])) <= 2 ** -7 * 3
+
+
+def test_worklist_entry_point_matches_fwd(gpu):
+    w = workloads.make_config(3)
+    say("[case] build_worklist + fwd_with_worklist vs fwd")
+    qkv, cu = to_gpu(w)
+    a = run_fwd(w, qkv=qkv, cu=cu)
+    items, count = vlca.build_worklist(cu, w.max_seqlen)
+    b = vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b.cpu())
+
+
+def test_int64_offsets_and_preallocated_out(gpu):
+    w = workloads.make_config(1)
+    qkv, cu = to_gpu(w)
+    a = run_fwd(w, qkv=qkv, cu=cu)
+    out = torch.full((w.total_tokens, 512), 7.0, dtype=torch.bfloat16, device="cuda")
+    r = vlca.fwd(qkv, cu.to(torch.int64), w.max_seqlen, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    assert r.data_ptr() == out.data_ptr()
+    assert torch.equal(a, out.cpu())
+
+
+def test_bad_shapes_raise(gpu):
+    w = workloads.make_config(1)
+    qkv, cu = to_gpu(w)
+    with pytest.raises(ValueError):
+        vlca.fwd(qkv[:, :1000], cu, 40)
+    with pytest.raises(ValueError):
+        vlca.fwd(qkv.float(), cu, 40)
+    with pytest.raises(vlca.VlcaError):
+        vlca.fwd(qkv, cu, 40, scale=-1.0)

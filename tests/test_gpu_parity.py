@@ -1,0 +1,91 @@
+"""HIP path vs the fp64 oracle, element by element (GPU).
+
+Small cases and the two smaller configurations compare every output element;
+the two large configurations compare a sample of rows the oracle evaluates one
+by one (tile edges, first/last rows of users, every row of short users, random
+rows), plus properties that hold at any size.  All runs use the same launch
+configuration as bench.py (varlen_causal_attn_fwd, persistent grid).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import assert_close, qkv64, run_fwd, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL_CASES = {
+    "tiny_1_7_16_40": dict(lengths=[1, 7, 16, 40]),
+    "plan_offsets_0_10_22_37": dict(lengths=workloads.PLAN_TEST_LENGTHS),
+    "tile_edges": dict(lengths=[63, 64, 65, 127, 128, 129, 1, 2]),
+    "zero_length_users": dict(lengths=[0, 5, 0, 0, 9, 1, 0, 200, 0]),
+    "single_user_1000": dict(lengths=[1000]),
+    "one_head": dict(lengths=[70, 3, 130], n_heads=1),
+    "three_heads": dict(lengths=[70, 3, 130, 64], n_heads=3),
+    "sixteen_heads": dict(lengths=[33, 190], n_heads=16),
+    "all_length_one": dict(lengths=[1] * 50),
+    "scaled_values_x4": dict(lengths=[90, 17], value_scale=4.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_small_cases_all_elements(gpu, name):
+    kw = SMALL_CASES[name]
+    say(f"[case] {name} {kw}")
+    w = workloads.make_from_lengths(kw["lengths"], seed=11, n_heads=kw.get("n_heads", 8),
+                                    value_scale=kw.get("value_scale", 1.0))
+    out = run_fwd(w)
+    ref = oracle.varlen_causal_attention(qkv64(w), w.cu_seqlens, w.n_heads, w.head_dim, w.scale)
+    # The output is linear in v: with v scaled by c the absolute bound (set for N(0,1)
+    # data) applies to out / c -- bf16's own rounding of |out| >= 8 exceeds it otherwise.
+    c = kw.get("value_scale", 1.0)
+    assert_close(out.double() / c, ref / c, name)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_configs_all_elements(gpu, idx):
+    w = workloads.make_config(idx)
+    say(f"[case] config {idx} {w.name} T={w.total_tokens} U={w.num_users}")
+    out = run_fwd(w)
+    ref = oracle.varlen_causal_attention(qkv64(w), w.cu_seqlens, w.n_heads, w.head_dim, w.scale)
+    assert_close(out, ref, w.name)
+
+
+def sample_rows(w, rng, per_long=160, max_short_rows=2500):
+    cu = w.cu_seqlens
+    rows = []
+    short_budget = max_short_rows
+    for u, L in enumerate(w.lengths):
+        s = int(cu[u])
+        if L <= 64 and short_budget > 0:
+            take = min(int(L), short_budget)
+            rows.extend(range(s, s + take))
+            short_budget -= take
+        elif L > 64:
+            cand = {0, int(L) - 1}
+            for t in range(64, int(L), 64):
+                cand.update({t - 1, t, min(t + 1, int(L) - 1)})
+            cand = sorted(cand)
+            if len(cand) > per_long // 2:
+                cand = list(rng.choice(cand, per_long // 2, replace=False))
+            cand += list(rng.integers(0, int(L), per_long // 2))
+            rows.extend(s + int(c) for c in cand)
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_configs_sampled_rows(gpu, idx):
+    w = workloads.make_config(idx)
+    say(f"[case] config {idx} {w.name} T={w.total_tokens} U={w.num_users} max_seqlen={w.max_seqlen}")
+    out = run_fwd(w)
+    assert np.all(np.isfinite(out.float().numpy()))
+    rows = sample_rows(w, np.random.default_rng(idx))
+    q = qkv64(w)
+    ref = oracle.varlen_causal_attention_rows(q, w.cu_seqlens, rows, w.n_heads, w.head_dim, w.scale)
+    assert_close(out[rows], ref, f"{w.name} ({rows.size} sampled rows)")
+    # every length-one user returns its own v row exactly
+    ones = w.cu_seqlens[:-1][w.lengths == 1]
+    if ones.size:
+        v = w.qkv_bf16[ones, 2 * w.n_heads * w.head_dim:]
+        assert (out[ones] == v).all()

@@ -252,3 +252,12 @@ def test_worklist_max_tiles_clamp():
     cu = workloads.cu_from_lengths([300, 10])
     got = oracle.reference_worklist(cu, 64, max_tiles=2)
     np.testing.assert_array_equal(got, [[0, 1], [0, 0], [1, 0]])
+
+
+def test_row_sampled_oracle_matches_full():
+    w = _rand_case([3, 0, 70, 1, 129], seed=12)
+    qkv = _qkv64(w)
+    full = oracle.varlen_causal_attention(qkv, w.cu_seqlens, H, D, w.scale)
+    rows = [0, 2, 3, 40, 72, 73, 74, 150, 201, 202]
+    part = oracle.varlen_causal_attention_rows(qkv, w.cu_seqlens, rows, H, D, w.scale)
+    assert np.max(np.abs(part - full[rows])) <= 1e-12

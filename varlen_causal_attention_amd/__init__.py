@@ -1,0 +1,186 @@
+"""Python binding of ``libvlca.so`` (gfx950 varlen causal attention forward).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (``include/varlen_causal_attn.h``).  torch supplies
+device memory and the current stream.  There is no fallback: if the library is
+not built, or a tensor is not on a ROCm device, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "VlcaError", "library", "library_path", "fwd", "build_worklist", "fwd_with_worklist",
+    "worklist_capacity", "tile_rows", "strerror", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libvlca.so")
+_lib = None
+
+EXPORTED_SYMBOLS = (
+    "varlen_causal_attn_fwd",
+    "varlen_causal_attn_worklist_capacity",
+    "varlen_causal_attn_build_worklist",
+    "varlen_causal_attn_fwd_worklist",
+    "varlen_causal_attn_tile_rows",
+    "varlen_causal_attn_strerror",
+)
+
+
+class VlcaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: error {code}: {strerror(code)}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """Load ``libvlca.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m varlen_causal_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32p, i64p = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
+    c_int, c_float = ctypes.c_int, ctypes.c_float
+    lib.varlen_causal_attn_fwd.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
+    lib.varlen_causal_attn_fwd.restype = c_int
+    lib.varlen_causal_attn_worklist_capacity.argtypes = [c_int, c_int, i64p]
+    lib.varlen_causal_attn_worklist_capacity.restype = c_int
+    lib.varlen_causal_attn_build_worklist.argtypes = [i32p, c_int, c_int, i32p, ctypes.c_int64, i32p, vp]
+    lib.varlen_causal_attn_build_worklist.restype = c_int
+    lib.varlen_causal_attn_fwd_worklist.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, i32p,
+                                                    ctypes.c_int64, vp, vp]
+    lib.varlen_causal_attn_fwd_worklist.restype = c_int
+    lib.varlen_causal_attn_tile_rows.argtypes = []
+    lib.varlen_causal_attn_tile_rows.restype = c_int
+    lib.varlen_causal_attn_strerror.argtypes = [c_int]
+    lib.varlen_causal_attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return library().varlen_causal_attn_strerror(int(code)).decode()
+
+
+def tile_rows() -> int:
+    return int(library().varlen_causal_attn_tile_rows())
+
+
+def worklist_capacity(num_users: int, max_seqlen: int) -> int:
+    cap = ctypes.c_int64(0)
+    rc = library().varlen_causal_attn_worklist_capacity(int(num_users), int(max_seqlen), ctypes.byref(cap))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_worklist_capacity")
+    return int(cap.value)
+
+
+def _stream_handle(device) -> int:
+    import torch
+
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_cu(cu_seqlens):
+    import torch
+
+    if not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D device tensor")
+    if cu_seqlens.dtype == torch.int64:
+        cu_seqlens = cu_seqlens.to(torch.int32)  # device-side conversion, no host sync
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32 or int64")
+    return cu_seqlens.contiguous()
+
+
+def _check_qkv(qkv, n_heads, head_dim):
+    import torch
+
+    if not qkv.is_cuda or qkv.dtype != torch.bfloat16 or qkv.dim() != 2:
+        raise ValueError("qkv must be a 2-D bfloat16 device tensor")
+    if qkv.shape[1] != 3 * n_heads * head_dim:
+        raise ValueError(f"qkv has {qkv.shape[1]} columns, expected 3*{n_heads}*{head_dim}")
+    if not qkv.is_contiguous():
+        raise ValueError("qkv must be contiguous")
+    if qkv.shape[0] >= 2**31:
+        raise ValueError("total tokens must be < 2^31")
+
+
+def _out_tensor(qkv, n_heads, head_dim, out):
+    import torch
+
+    shape = (qkv.shape[0], n_heads * head_dim)
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=qkv.device)
+    if tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != qkv.device:
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {shape} on {qkv.device}")
+    return out
+
+
+def fwd(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
+        scale: Optional[float] = None, out=None):
+    """Block-diagonal causal attention over packed users; returns ``out`` [T, n_heads*head_dim] bf16.
+
+    ``max_seqlen`` is an upper bound on every user's length (a bucket constant is
+    fine).  The call is asynchronous on torch's current stream.
+    """
+    _check_qkv(qkv, n_heads, head_dim)
+    cu = _check_cu(cu_seqlens)
+    out = _out_tensor(qkv, n_heads, head_dim, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    rc = library().varlen_causal_attn_fwd(qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1, int(max_seqlen),
+                                          int(n_heads), int(head_dim), float(scale), out.data_ptr(),
+                                          _stream_handle(qkv.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_fwd")
+    return out
+
+
+def build_worklist(cu_seqlens, max_seqlen: int) -> Tuple["object", "object"]:
+    """Run the segment scheduler alone; returns (items int32 [capacity, 4], count int32 [1]) on the device.
+
+    Rows ``items[:count]`` are (user, q_tile, row_start, length), longest q-tile first.
+    """
+    import torch
+
+    cu = _check_cu(cu_seqlens)
+    cap = worklist_capacity(cu.shape[0] - 1, max_seqlen)
+    items = torch.empty((cap, 4), dtype=torch.int32, device=cu.device)
+    count = torch.empty((1,), dtype=torch.int32, device=cu.device)
+    rc = library().varlen_causal_attn_build_worklist(cu.data_ptr(), cu.shape[0] - 1, int(max_seqlen),
+                                                     items.data_ptr(), cap, count.data_ptr(),
+                                                     _stream_handle(cu.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_build_worklist")
+    return items, count
+
+
+def fwd_with_worklist(qkv, cu_seqlens, max_seqlen: int, items, n_heads: int = 8, head_dim: int = 64,
+                      scale: Optional[float] = None, out=None):
+    """Attention kernel alone over a worklist from :func:`build_worklist` (same cu_seqlens/max_seqlen)."""
+    import torch
+
+    _check_qkv(qkv, n_heads, head_dim)
+    cu = _check_cu(cu_seqlens)
+    if items.dtype != torch.int32 or items.dim() != 2 or items.shape[1] != 4 or not items.is_contiguous():
+        raise ValueError("items must be a contiguous int32 [capacity, 4] tensor")
+    out = _out_tensor(qkv, n_heads, head_dim, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    rc = library().varlen_causal_attn_fwd_worklist(qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1,
+                                                   int(max_seqlen), int(n_heads), int(head_dim), float(scale),
+                                                   items.data_ptr(), items.shape[0], out.data_ptr(),
+                                                   _stream_handle(qkv.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_fwd_worklist")
+    return out

@@ -1,0 +1,189 @@
+// C ABI of the varlen causal attention library: argument checks (all on the
+// host, before any HIP call), the per-(device, stream) scheduler workspace, and
+// the launches.  Declarations and the full contract are in
+// include/varlen_causal_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "varlen_causal_attn.h"
+#include "vlca_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Workspace {
+  int4* items = nullptr;     // capacity items, then one int32 count
+  int64_t capacity = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
+std::map<int, int> g_cu_count;
+
+int64_t max_tiles_of(int max_seqlen) { return (static_cast<int64_t>(max_seqlen) + vlca::kTileRows - 1) / vlca::kTileRows; }
+
+int64_t required_capacity(int num_users, int max_seqlen) {
+  return static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen) + vlca::kWorklistTail;
+}
+
+// Size and scalar checks shared by every entry point.
+int check_sizes(int num_users, int max_seqlen) {
+  if (num_users < 0 || max_seqlen < 0) return VLCA_ERR_NEGATIVE_SIZE;
+  if (max_seqlen > VLCA_MAX_SEQLEN) return VLCA_ERR_TOO_LARGE;
+  if (required_capacity(num_users, max_seqlen) > INT32_MAX) return VLCA_ERR_TOO_LARGE;
+  return VLCA_OK;
+}
+
+int check_attention_args(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads,
+                         int head_dim, float scale, const void* out) {
+  int rc = check_sizes(num_users, max_seqlen);
+  if (rc != VLCA_OK) return rc;
+  if (head_dim != vlca::kHeadDim) return VLCA_ERR_HEAD_DIM;
+  if (n_heads < 1 || n_heads > 65536) return VLCA_ERR_N_HEADS;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return VLCA_ERR_SCALE;
+  if (num_users > 0 && (qkv == nullptr || cu_seqlens == nullptr || out == nullptr)) return VLCA_ERR_NULL_POINTER;
+  if (qkv != nullptr && qkv == out) return VLCA_ERR_ALIAS;
+  return VLCA_OK;
+}
+
+int cu_count(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cu_count.find(dev);
+  if (it != g_cu_count.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_cu_count[dev] = n;
+  return n;
+}
+
+int grid_size(int dev, int num_users, int max_seqlen, int n_heads) {
+  int64_t g = static_cast<int64_t>(cu_count(dev)) * vlca::kBlocksPerCU;
+  if (g > vlca::kMaxGrid) g = vlca::kMaxGrid;
+  g -= g % 8;  // keeps w % 8 == blockIdx.x % 8 (one head per XCD when H = 8)
+  if (g < 8) g = 8;
+  const int64_t work = static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen) * n_heads;
+  if (work < g) g = work;
+  return static_cast<int>(g);
+}
+
+// Workspace for (device, stream), grown when a call needs more items.  Growth
+// synchronises `stream` before freeing the old buffer, so it is refused while
+// the stream is capturing.
+int get_workspace(int dev, hipStream_t stream, int64_t capacity, Workspace** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& ws = g_workspaces[std::make_pair(dev, stream)];
+  if (ws.capacity < capacity) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return VLCA_ERR_HIP;
+    if (st != hipStreamCaptureStatusNone) return VLCA_ERR_WORKSPACE;
+    int64_t cap = ws.capacity > 0 ? ws.capacity : 65536;
+    while (cap < capacity) cap *= 2;
+    if (ws.items != nullptr) {
+      if (hipStreamSynchronize(stream) != hipSuccess) return VLCA_ERR_HIP;
+      (void)hipFree(ws.items);
+      ws.items = nullptr;
+      ws.capacity = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, static_cast<size_t>(cap) * sizeof(int4) + 256) != hipSuccess) return VLCA_ERR_WORKSPACE;
+    ws.items = static_cast<int4*>(p);
+    ws.capacity = cap;
+  }
+  *out = &ws;
+  return VLCA_OK;
+}
+
+int32_t* workspace_count(const Workspace* ws) { return reinterpret_cast<int32_t*>(ws->items + ws->capacity); }
+
+int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, float scale,
+                const int4* items, int4* items_w, int32_t* count, void* out, hipStream_t stream, bool schedule) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  if (schedule) {
+    if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items_w, count, stream) != hipSuccess)
+      return VLCA_ERR_HIP;
+  }
+  const int grid = grid_size(dev, num_users, max_seqlen, n_heads);
+  if (vlca::launch_attention(qkv, items, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
+    return VLCA_ERR_HIP;
+  return VLCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads,
+                           int head_dim, float scale, void* out, hipStream_t stream) {
+  int rc = check_attention_args(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out);
+  if (rc != VLCA_OK) return rc;
+  if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  Workspace* ws = nullptr;
+  rc = get_workspace(dev, stream, required_capacity(num_users, max_seqlen), &ws);
+  if (rc != VLCA_OK) return rc;
+  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, ws->items, ws->items,
+                     workspace_count(ws), out, stream, true);
+}
+
+int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity) {
+  int rc = check_sizes(num_users, max_seqlen);
+  if (rc != VLCA_OK) return rc;
+  if (capacity == nullptr) return VLCA_ERR_NULL_POINTER;
+  *capacity = required_capacity(num_users, max_seqlen);
+  return VLCA_OK;
+}
+
+int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, int max_seqlen, int32_t* items,
+                                      int64_t capacity, int32_t* count, hipStream_t stream) {
+  int rc = check_sizes(num_users, max_seqlen);
+  if (rc != VLCA_OK) return rc;
+  if (items == nullptr || count == nullptr || (num_users > 0 && cu_seqlens == nullptr)) return VLCA_ERR_NULL_POINTER;
+  if (capacity < required_capacity(num_users, max_seqlen)) return VLCA_ERR_CAPACITY;
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, reinterpret_cast<int4*>(items), count, stream) !=
+      hipSuccess)
+    return VLCA_ERR_HIP;
+  return VLCA_OK;
+}
+
+int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
+                                    int n_heads, int head_dim, float scale, const int32_t* items, int64_t capacity,
+                                    void* out, hipStream_t stream) {
+  int rc = check_attention_args(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out);
+  if (rc != VLCA_OK) return rc;
+  if (num_users > 0 && items == nullptr) return VLCA_ERR_NULL_POINTER;
+  if (num_users > 0 && capacity < required_capacity(num_users, max_seqlen)) return VLCA_ERR_CAPACITY;
+  if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
+  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, reinterpret_cast<const int4*>(items),
+                     nullptr, nullptr, out, stream, false);
+}
+
+int varlen_causal_attn_tile_rows(void) { return vlca::kTileRows; }
+
+const char* varlen_causal_attn_strerror(int code) {
+  switch (code) {
+    case VLCA_OK: return "success";
+    case VLCA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case VLCA_ERR_NEGATIVE_SIZE: return "num_users or max_seqlen is negative";
+    case VLCA_ERR_HEAD_DIM: return "head_dim must be 64";
+    case VLCA_ERR_N_HEADS: return "n_heads must be in [1, 65536]";
+    case VLCA_ERR_SCALE: return "scale must be finite and > 0";
+    case VLCA_ERR_TOO_LARGE: return "max_seqlen exceeds VLCA_MAX_SEQLEN or the worklist exceeds 2^31 items";
+    case VLCA_ERR_CAPACITY: return "worklist buffer is smaller than varlen_causal_attn_worklist_capacity()";
+    case VLCA_ERR_ALIAS: return "qkv and out must not be the same buffer";
+    case VLCA_ERR_WORKSPACE: return "library workspace could not be allocated (or must grow during stream capture)";
+    case VLCA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,25 @@
+// Internal launch interface between the C ABI (vlca_api.cpp) and the gfx950
+// kernels (vlca_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vlca {
+
+constexpr int kTileRows = 64;        // query rows per work item == keys per K/V tile
+constexpr int kHeadDim = 64;
+constexpr int kMaxLevels = 4096;     // q-tiles per user the scheduler can order
+constexpr int kWorklistTail = 4096;  // sentinel items after the last real item
+constexpr int kMaxGrid = 2048;       // persistent grid cap (< kWorklistTail)
+constexpr int kBlocksPerCU = 4;      // attention workgroups resident per CU
+
+// Scheduler: one workgroup builds the (user, q_tile, row_start, length) list.
+hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles,
+                           int4* items, int32_t* count, hipStream_t stream);
+
+// Attention: persistent grid walking the worklist (heads fastest).
+hipError_t launch_attention(const void* qkv, const int4* items, int n_heads, float scale_log2e,
+                            void* out, int grid, hipStream_t stream);
+
+}  // namespace vlca
