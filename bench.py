@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = 6823 tokens / 60 users)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB --steps times (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -109,6 +111,17 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return
     w = workloads.make_config(args.config)
     qkv = w.qkv_bf16.to(dev)
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
@@ -139,11 +152,11 @@ def main():
     # back to back on the same stream, timed with events on that stream.
     items, _count = vlca.build_worklist(cu, w.max_seqlen)
     for _ in range(args.warmup):
-        vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, scale=w.scale, out=out)
+        vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, _count, scale=w.scale, out=out)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, scale=w.scale, out=out)
+        vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, _count, scale=w.scale, out=out)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_attn = e0.elapsed_time(e1) / args.steps

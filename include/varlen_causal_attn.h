@@ -55,7 +55,6 @@ typedef struct ihipStream_t* hipStream_t;
 
 #define VLCA_TILE_ROWS 64          /* query rows per work item, keys per K/V tile  */
 #define VLCA_MAX_SEQLEN 262144     /* max_seqlen upper limit (4096 q-tiles a user) */
-#define VLCA_WORKLIST_TAIL 4096    /* sentinel items written after the last item   */
 
 enum {
   VLCA_OK = 0,
@@ -96,8 +95,8 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
 
 /*
  * Worklist size (in items) needed by varlen_causal_attn_build_worklist and
- * varlen_causal_attn_fwd_worklist: num_users*ceil(max_seqlen/64) + VLCA_WORKLIST_TAIL.
- * Pure host arithmetic.  Writes it to *capacity.
+ * varlen_causal_attn_fwd_worklist: num_users*ceil(max_seqlen/64).  Pure host
+ * arithmetic.  Writes it to *capacity.
  */
 int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity);
 
@@ -106,9 +105,10 @@ int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t*
  * `stream`, the compact worklist for 64-row q-tiles: items[4*i .. 4*i+3] =
  * (user, q_tile, row_start, length) for i < *count, ordered by q_tile
  * descending and, within one q_tile, by user ascending; users with no rows give
- * no items.  Items [*count, *count + VLCA_WORKLIST_TAIL) are sentinels
- * (-1, -1, 0, 0).  A user's tile count is clamped to ceil(max_seqlen/64).
- *   items     device, int32 [capacity][4], caller-owned
+ * no items; entries from *count on are left untouched.  A user's tile count is
+ * clamped to ceil(max_seqlen/64).
+ *   items     device, int32 [capacity][4], caller-owned (may be NULL if capacity
+ *             needed is 0)
  *   capacity  items available; must be >= varlen_causal_attn_worklist_capacity()
  *   count     device, int32 [1], caller-owned: number of items
  */
@@ -118,15 +118,16 @@ int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, 
 
 /*
  * Attention kernel alone, over a worklist that varlen_causal_attn_build_worklist
- * wrote (same cu_seqlens, num_users, max_seqlen) earlier in stream order.  Uses
- * no library workspace, so it may be captured in a HIP graph together with the
- * scheduler call.  Arguments as for varlen_causal_attn_fwd, plus the caller's
- * items/capacity buffer.
+ * wrote (same cu_seqlens, num_users, max_seqlen) earlier in stream order; the
+ * kernel reads *count on the device.  Uses no library workspace, so it may be
+ * captured in a HIP graph together with the scheduler call, and one worklist can
+ * serve several calls over the same batch (e.g. every layer of a model).
+ * Arguments as for varlen_causal_attn_fwd, plus the caller's items/capacity/count.
  */
 int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, int num_users,
                                     int max_seqlen, int n_heads, int head_dim, float scale,
-                                    const int32_t* items, int64_t capacity, void* out,
-                                    hipStream_t stream);
+                                    const int32_t* items, int64_t capacity, const int32_t* count,
+                                    void* out, hipStream_t stream);
 
 /* Query rows per work item (and keys per K/V tile): VLCA_TILE_ROWS. */
 int varlen_causal_attn_tile_rows(void);

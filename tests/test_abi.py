@@ -49,9 +49,9 @@ def test_constants_and_strings():
 
 
 def test_worklist_capacity():
-    assert vlca.worklist_capacity(60, 452) == 60 * 8 + 4096
-    assert vlca.worklist_capacity(0, 0) == 4096
-    assert vlca.worklist_capacity(1000, 4096) == 1000 * 64 + 4096
+    assert vlca.worklist_capacity(60, 452) == 60 * 8
+    assert vlca.worklist_capacity(0, 0) == 0
+    assert vlca.worklist_capacity(1000, 4096) == 1000 * 64
     with pytest.raises(vlca.VlcaError) as e:
         vlca.worklist_capacity(-1, 10)
     assert e.value.code == -2
@@ -102,11 +102,12 @@ def test_build_worklist_and_fwd_worklist_validation():
     assert lib.varlen_causal_attn_build_worklist(FAKE, 4, 40, None, 5000, FAKE, None) == -1
     assert lib.varlen_causal_attn_build_worklist(FAKE, 4, 40, FAKE, 5000, None, None) == -1
     assert lib.varlen_causal_attn_build_worklist(None, 4, 40, FAKE, 5000, FAKE, None) == -1
-    assert lib.varlen_causal_attn_build_worklist(FAKE, 4, 40, FAKE, 4099, FAKE, None) == -7
+    assert lib.varlen_causal_attn_build_worklist(FAKE, 4, 40, FAKE, 3, FAKE, None) == -7
     assert lib.varlen_causal_attn_build_worklist(FAKE, -4, 40, FAKE, 9999, FAKE, None) == -2
     f = lib.varlen_causal_attn_fwd_worklist
     c = ctypes.c_float(0.125)
-    assert f(FAKE, FAKE, 4, 40, 8, 64, c, None, 5000, FAKE * 2, None) == -1
-    assert f(FAKE, FAKE, 4, 40, 8, 64, c, FAKE, 4099, FAKE * 2, None) == -7
-    assert f(FAKE, FAKE, 4, 40, 8, 96, c, FAKE, 5000, FAKE * 2, None) == -3
-    assert f(None, None, 0, 40, 8, 64, c, None, 0, None, None) == 0
+    assert f(FAKE, FAKE, 4, 40, 8, 64, c, None, 5000, FAKE, FAKE * 2, None) == -1
+    assert f(FAKE, FAKE, 4, 40, 8, 64, c, FAKE, 5000, None, FAKE * 2, None) == -1
+    assert f(FAKE, FAKE, 4, 40, 8, 64, c, FAKE, 3, FAKE, FAKE * 2, None) == -7
+    assert f(FAKE, FAKE, 4, 40, 8, 96, c, FAKE, 5000, FAKE, FAKE * 2, None) == -3
+    assert f(None, None, 0, 40, 8, 64, c, None, 0, None, None, None) == 0

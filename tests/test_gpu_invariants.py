@@ -112,7 +112,7 @@ def test_worklist_entry_point_matches_fwd(gpu):
     qkv, cu = to_gpu(w)
     a = run_fwd(w, qkv=qkv, cu=cu)
     items, count = vlca.build_worklist(cu, w.max_seqlen)
-    b = vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, scale=w.scale)
+    b = vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, count, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b.cpu())
 

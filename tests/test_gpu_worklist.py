@@ -28,9 +28,6 @@ def check(cu_np, max_seqlen, label):
     cu = np.asarray(cu_np, dtype=np.int64)
     np.testing.assert_array_equal(items[:n, 2], cu[ref[:, 0]])
     np.testing.assert_array_equal(items[:n, 3], cu[ref[:, 0] + 1] - cu[ref[:, 0]])
-    tail = items[n:n + 4096]
-    assert tail.shape[0] == 4096
-    assert (tail[:, 0] == -1).all() and (tail[:, 1] == -1).all()
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
@@ -61,7 +58,7 @@ def test_clamped_to_max_seqlen(gpu):
 
 def test_empty_and_all_zero(gpu):
     items, n = gpu_worklist([0], 64)
-    assert n == 0 and (items[:4096, 0] == -1).all()
+    assert n == 0 and items.shape[0] == 0
     check(workloads.cu_from_lengths([0, 0, 0]), 64, "all zero")
 
 

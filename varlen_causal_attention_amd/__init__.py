@@ -58,7 +58,7 @@ def library():
     lib.varlen_causal_attn_build_worklist.argtypes = [i32p, c_int, c_int, i32p, ctypes.c_int64, i32p, vp]
     lib.varlen_causal_attn_build_worklist.restype = c_int
     lib.varlen_causal_attn_fwd_worklist.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, i32p,
-                                                    ctypes.c_int64, vp, vp]
+                                                    ctypes.c_int64, i32p, vp, vp]
     lib.varlen_causal_attn_fwd_worklist.restype = c_int
     lib.varlen_causal_attn_tile_rows.argtypes = []
     lib.varlen_causal_attn_tile_rows.restype = c_int
@@ -149,7 +149,8 @@ def fwd(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
 def build_worklist(cu_seqlens, max_seqlen: int) -> Tuple["object", "object"]:
     """Run the segment scheduler alone; returns (items int32 [capacity, 4], count int32 [1]) on the device.
 
-    Rows ``items[:count]`` are (user, q_tile, row_start, length), longest q-tile first.
+    Rows ``items[:count]`` are (user, q_tile, row_start, length), longest q-tile first;
+    later rows are unspecified.
     """
     import torch
 
@@ -165,7 +166,7 @@ def build_worklist(cu_seqlens, max_seqlen: int) -> Tuple["object", "object"]:
     return items, count
 
 
-def fwd_with_worklist(qkv, cu_seqlens, max_seqlen: int, items, n_heads: int = 8, head_dim: int = 64,
+def fwd_with_worklist(qkv, cu_seqlens, max_seqlen: int, items, count, n_heads: int = 8, head_dim: int = 64,
                       scale: Optional[float] = None, out=None):
     """Attention kernel alone over a worklist from :func:`build_worklist` (same cu_seqlens/max_seqlen)."""
     import torch
@@ -174,13 +175,15 @@ def fwd_with_worklist(qkv, cu_seqlens, max_seqlen: int, items, n_heads: int = 8,
     cu = _check_cu(cu_seqlens)
     if items.dtype != torch.int32 or items.dim() != 2 or items.shape[1] != 4 or not items.is_contiguous():
         raise ValueError("items must be a contiguous int32 [capacity, 4] tensor")
+    if count.dtype != torch.int32 or count.numel() != 1 or not count.is_cuda:
+        raise ValueError("count must be a device int32 tensor with one element")
     out = _out_tensor(qkv, n_heads, head_dim, out)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     rc = library().varlen_causal_attn_fwd_worklist(qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1,
                                                    int(max_seqlen), int(n_heads), int(head_dim), float(scale),
-                                                   items.data_ptr(), items.shape[0], out.data_ptr(),
-                                                   _stream_handle(qkv.device))
+                                                   items.data_ptr(), items.shape[0], count.data_ptr(),
+                                                   out.data_ptr(), _stream_handle(qkv.device))
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd_worklist")
     return out

@@ -17,8 +17,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvlca.so")
 SOURCES = [os.path.join(CSRC, "vlca_kernels.hip"), os.path.join(CSRC, "vlca_api.cpp")]
 
-# Packed fp32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are disabled for all device code.  MFMA results are kept
+# in VGPRs (not AGPRs): the softmax reads every score and rescales the
+# accumulators, and AGPR results would need a v_accvgpr copy each way.
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def hipcc() -> str:

@@ -29,7 +29,7 @@ std::map<int, int> g_cu_count;
 int64_t max_tiles_of(int max_seqlen) { return (static_cast<int64_t>(max_seqlen) + vlca::kTileRows - 1) / vlca::kTileRows; }
 
 int64_t required_capacity(int num_users, int max_seqlen) {
-  return static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen) + vlca::kWorklistTail;
+  return static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen);
 }
 
 // Size and scalar checks shared by every entry point.
@@ -82,7 +82,7 @@ int get_workspace(int dev, hipStream_t stream, int64_t capacity, Workspace** out
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &st) != hipSuccess) return VLCA_ERR_HIP;
     if (st != hipStreamCaptureStatusNone) return VLCA_ERR_WORKSPACE;
-    int64_t cap = ws.capacity > 0 ? ws.capacity : 65536;
+    int64_t cap = ws.capacity > 0 ? ws.capacity : 16384;
     while (cap < capacity) cap *= 2;
     if (ws.items != nullptr) {
       if (hipStreamSynchronize(stream) != hipSuccess) return VLCA_ERR_HIP;
@@ -102,16 +102,16 @@ int get_workspace(int dev, hipStream_t stream, int64_t capacity, Workspace** out
 int32_t* workspace_count(const Workspace* ws) { return reinterpret_cast<int32_t*>(ws->items + ws->capacity); }
 
 int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, float scale,
-                const int4* items, int4* items_w, int32_t* count, void* out, hipStream_t stream, bool schedule) {
+                int4* items, int32_t* count, void* out, hipStream_t stream, bool schedule) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   if (schedule) {
-    if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items_w, count, stream) != hipSuccess)
+    if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items, count, stream) != hipSuccess)
       return VLCA_ERR_HIP;
   }
   const int grid = grid_size(dev, num_users, max_seqlen, n_heads);
-  if (vlca::launch_attention(qkv, items, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
+  if (vlca::launch_attention(qkv, items, count, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
@@ -130,8 +130,8 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   Workspace* ws = nullptr;
   rc = get_workspace(dev, stream, required_capacity(num_users, max_seqlen), &ws);
   if (rc != VLCA_OK) return rc;
-  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, ws->items, ws->items,
-                     workspace_count(ws), out, stream, true);
+  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, ws->items, workspace_count(ws), out,
+                     stream, true);
 }
 
 int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity) {
@@ -146,8 +146,10 @@ int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, 
                                       int64_t capacity, int32_t* count, hipStream_t stream) {
   int rc = check_sizes(num_users, max_seqlen);
   if (rc != VLCA_OK) return rc;
-  if (items == nullptr || count == nullptr || (num_users > 0 && cu_seqlens == nullptr)) return VLCA_ERR_NULL_POINTER;
-  if (capacity < required_capacity(num_users, max_seqlen)) return VLCA_ERR_CAPACITY;
+  const int64_t need = required_capacity(num_users, max_seqlen);
+  if (count == nullptr || (need > 0 && items == nullptr) || (num_users > 0 && cu_seqlens == nullptr))
+    return VLCA_ERR_NULL_POINTER;
+  if (capacity < need) return VLCA_ERR_CAPACITY;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, reinterpret_cast<int4*>(items), count, stream) !=
       hipSuccess)
@@ -157,14 +159,15 @@ int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, 
 
 int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
                                     int n_heads, int head_dim, float scale, const int32_t* items, int64_t capacity,
-                                    void* out, hipStream_t stream) {
+                                    const int32_t* count, void* out, hipStream_t stream) {
   int rc = check_attention_args(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out);
   if (rc != VLCA_OK) return rc;
-  if (num_users > 0 && items == nullptr) return VLCA_ERR_NULL_POINTER;
+  if (num_users > 0 && (items == nullptr || count == nullptr)) return VLCA_ERR_NULL_POINTER;
   if (num_users > 0 && capacity < required_capacity(num_users, max_seqlen)) return VLCA_ERR_CAPACITY;
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
-  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, reinterpret_cast<const int4*>(items),
-                     nullptr, nullptr, out, stream, false);
+  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale,
+                     reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), out, stream,
+                     false);
 }
 
 int varlen_causal_attn_tile_rows(void) { return vlca::kTileRows; }

@@ -10,16 +10,16 @@ namespace vlca {
 constexpr int kTileRows = 64;        // query rows per work item == keys per K/V tile
 constexpr int kHeadDim = 64;
 constexpr int kMaxLevels = 4096;     // q-tiles per user the scheduler can order
-constexpr int kWorklistTail = 4096;  // sentinel items after the last real item
-constexpr int kMaxGrid = 2048;       // persistent grid cap (< kWorklistTail)
-constexpr int kBlocksPerCU = 4;      // attention workgroups resident per CU
+constexpr int kStages = 3;           // K/V tile ring depth in LDS (16 KB per stage)
+constexpr int kBlocksPerCU = 3;      // attention workgroups resident per CU (LDS-limited)
+constexpr int kMaxGrid = 4096;       // persistent grid cap
 
 // Scheduler: one workgroup builds the (user, q_tile, row_start, length) list.
 hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles,
                            int4* items, int32_t* count, hipStream_t stream);
 
-// Attention: persistent grid walking the worklist (heads fastest).
-hipError_t launch_attention(const void* qkv, const int4* items, int n_heads, float scale_log2e,
-                            void* out, int grid, hipStream_t stream);
+// Attention: persistent grid walking the first *count items (heads fastest).
+hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int n_heads,
+                            float scale_log2e, void* out, int grid, hipStream_t stream);
 
 }  // namespace vlca

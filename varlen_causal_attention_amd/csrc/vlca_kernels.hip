@@ -19,14 +19,24 @@
 //    later q-tiles of the same user.
 //
 // Attention workgroup: 4 waves; wave w owns query rows 16w..16w+15 of the tile.
-// Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16
-// (A = K rows from LDS, B = Q held in registers), so each lane holds 4 keys of a
-// single query per 16x16 block: the row max and row sum are in-lane work plus two
-// cross-lane steps, and the rescale factor is a per-lane scalar.  P^T stays in
-// registers and feeds O^T = V^T P^T directly as the B operand; V is staged in LDS
-// transposed ([dim][key]) with keys permuted so that each A fragment is one
-// 16-byte LDS read.  K/V tiles are double-buffered in LDS; the next tile's
-// global loads are issued before the current tile's MFMAs.
+//  * K and V tiles (64 keys x 64 dims, 8 KB each) are copied from HBM straight
+//    into LDS with global_load_lds_dwordx4 (no VGPRs, no VALU), through a ring of
+//    kStages buffers, so kStages-1 tiles are in flight while one is consumed.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16
+//    (A = K rows from LDS, B = Q held in registers): a lane holds 4 keys of one
+//    query per 16x16 block, so the row max is in-lane work plus two cross-lane
+//    steps and every per-row factor is a per-lane scalar.
+//  * P^T stays in registers and is the B operand of O^T = V^T P^T.  The A operand
+//    (V^T) is read from the natural [key][dim] V tile with ds_read_b64_tr_b16:
+//    within each 16-lane group, lane i gets element i%4 of source lanes
+//    {i/4, 4+i/4, 8+i/4, 12+i/4}; if source lane j points at key row j/4, dims
+//    4(j%4)..4(j%4)+3, lane i receives 4 consecutive keys of dim i.  The rows of
+//    each S^T block are permuted so that P^T comes out in that key order.
+//  * The softmax denominator is one more MFMA per 32 keys: an all-ones A operand
+//    times P^T sums the same bf16-rounded weights that multiply V.
+//  * The running max is only raised when a tile's max exceeds it by more than
+//    2^kRescaleLog2 in exp2 units; weights stay <= 2^8 and the rescale of acc (a
+//    wave-uniform branch) is skipped on almost every tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,15 +46,27 @@ namespace vlca {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define LDS __attribute__((address_space(3)))
+typedef LDS bf16x4 lds_bf16x4;
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedCache = 8160;  // cu_seqlens entries cached in LDS by the scheduler (LDS <= 64 KB)
-constexpr int kAttnThreads = 256;
-constexpr int kLdsRow = 72;        // bf16 per LDS tile row: 64 + 8 pad (144 B, 16 B aligned)
-constexpr int kTileElems = kTileRows * kLdsRow;
+#ifndef VLCA_QUERY_BLOCKS_PER_WAVE
+#define VLCA_QUERY_BLOCKS_PER_WAVE 1
+#endif
+constexpr int kQB = VLCA_QUERY_BLOCKS_PER_WAVE;        // 16-row query blocks per wave (1, 2 or 4)
+constexpr int kRowsPerWave = 16 * kQB;
+constexpr int kWaves = kTileRows / kRowsPerWave;       // waves per workgroup
+constexpr int kAttnThreads = 64 * kWaves;
+constexpr int kCopyInstr = kRowsPerWave / 8;           // 1 KB copy instructions per wave per 8 KB tile
+constexpr int kTileBytes = kTileRows * kHeadDim * 2;  // 8 KB: one 64 x 64 bf16 tile, 128 B rows
+constexpr int kStageBytes = 2 * kTileBytes;           // K tile then V tile
+constexpr float kRescaleLog2 = 8.0f;
 
 // ----------------------------------------------------------------- scheduler
 
@@ -152,26 +174,38 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
       slot += __popcll(m);
     }
   }
-  const int n = s_total;
-  if (tid == 0) *count = n;
-  for (int i = tid; i < kWorklistTail; i += kSchedThreads) items[n + i] = make_int4(-1, -1, 0, 0);
+  if (tid == 0) *count = s_total;
 }
 
 // ----------------------------------------------------------------- attention
 
-// Position of tile-local key kk (0..63) inside a V^T LDS row.  Within each
-// 32-key half, lane group g (lanes 16g..16g+15) needs keys {4g..4g+3} and
-// {16+4g..16+4g+3} as its 8 consecutive MFMA k-slots; storing them contiguously
-// makes each V^T fragment a single 16-byte read.
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int half = kk >> 5, k = kk & 31;
-  return (half << 5) | (((k & 15) >> 2) << 3) | ((k >> 4) << 2) | (k & 3);
-}
+// XOR swizzles of the 16-byte chunk index inside a 128-byte LDS tile row, chosen
+// so that the fragment reads below touch distinct banks (checked for both 32 and
+// 64 four-byte banks).  K rows are read 16 at a time as rows 8a+4e+{0..3}
+// (a = 0..3); V rows 4 at a time per 16-lane group as rows 8g+{0..3}.
+__device__ __forceinline__ int swz_k(int r) { return ((r & 3) ^ ((r >> 4) & 1)) | (((r >> 3) & 1) << 2); }
+__device__ __forceinline__ int swz_v(int r) { return ((r & 3) ^ ((r >> 3) & 1)) << 1; }
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+// LDS reads go through address-space-3 pointers derived from the stage object
+// itself, so the compiler can see which copies they may depend on.
+__device__ __forceinline__ bf16x8 lds_b128(const LDS char* base, int byte_off) {
+  return __builtin_bit_cast(bf16x8, *(const LDS u32x4*)(base + byte_off));
+}
+
+__device__ __forceinline__ bf16x4 lds_tr16(const LDS char* base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + byte_off));
+}
+
+// Max over lanes l, l^16, l^32, l^48 (the 4 lane groups holding one query's keys),
+// with the gfx950 row-swap permutes: each lane ends up holding its own value and
+// its partner's, so the max of the pair is the pairwise max.
+__device__ __forceinline__ float max_across_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -179,174 +213,341 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // RNE
 }
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Wait until at most n vector-memory operations of this wave are outstanding and
+// all of its LDS operations have completed.  An asm statement with a "memory"
+// clobber, so no memory access is moved across it.
+template <int n>
+__device__ __forceinline__ void wait_vmem_lds() {
+  static_assert(n >= 0 && n < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(n) : "memory");
+}
+
+// The same wait followed by a workgroup barrier.  __syncthreads() would add a
+// release fence that also waits for every LDS copy still in flight, draining the
+// tile ring; here only what the caller names (n copies may stay in flight).
+template <int n>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
+// Copy 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
+// lane l reads base + voff (a wave-uniform 64-bit base, a per-lane 32-bit byte
+// offset) and its bytes land at lds_wave_base + 16*l.  Issued from inline asm so
+// that the compiler, which would otherwise track these LDS writes coarsely and
+// insert waits for every copy in flight before unrelated LDS reads, leaves all
+// waits on them to the explicit wait_vmem_lds / wait_and_barrier calls.  The
+// instruction has no register result; M0 (the LDS base operand) is saved and
+// restored around it.
+__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, const LDS void* lds_wave_base) {
+  // readfirstlane returns int: widen through uint32_t so the low word is not
+  // sign-extended into the high word of the 64-bit base.
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
+  const uint64_t sbase = (uint64_t)lo | ((uint64_t)hi << 32);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+// One ring stage: the K tile then the V tile.
+struct Stage {
+  char bytes[kStageBytes];
+};
+
+// Per-lane constants of the attention workgroup.  Wave w owns query rows
+// kRowsPerWave*w .. kRowsPerWave*(w+1)-1 of the 64-row tile, as kQB blocks of 16;
+// it also copies those rows of every K, V and Q tile into LDS.
+struct Lanes {
+  int g, lq, wid, lane;
+  int qr[kQB];                       // query row (inside the tile) of block qb
+  int crow[kCopyInstr];              // tile row copied by this lane, per instruction
+  int ck[kCopyInstr], cv[kCopyInstr];  // logical 16-byte chunk copied (K/Q and V swizzle)
+  uint32_t kofs_g[kCopyInstr], vofs_g[kCopyInstr];  // byte offset of that chunk from the tile's first row
+  int kofs[4][2];                    // K fragment byte offsets inside a stage
+  int vofs[2][4][2];                 // V^T fragment byte offsets inside a stage
+};
+
+__device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
+  const int tid = threadIdx.x;
+  L.lane = tid & 63;
+  L.wid = tid >> 6;
+  L.g = L.lane >> 4;
+  L.lq = L.lane & 15;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) L.qr[qb] = L.wid * kRowsPerWave + 16 * qb + L.lq;
+  // Copy role: instruction i moves tile rows kRowsPerWave*wid + 8i .. +7; lane l
+  // lands at byte 16*l of that 1 KB slice (row l/8, physical chunk l%8).
+  const int cpos = L.lane & 7;
+#pragma unroll
+  for (int i = 0; i < kCopyInstr; ++i) {
+    L.crow[i] = kRowsPerWave * L.wid + 8 * i + (L.lane >> 3);
+    L.ck[i] = cpos ^ swz_k(L.crow[i]);
+    L.cv[i] = cpos ^ swz_v(L.crow[i]);
+    L.kofs_g[i] = (uint32_t)(L.crow[i] * ldq * 2 + 16 * L.ck[i]);
+    L.vofs_g[i] = (uint32_t)(L.crow[i] * ldq * 2 + 16 * L.cv[i]);
+  }
+  // K fragment rows: S^T block b (keys 32h..32h+31 with h = b/2, e = b%2), MFMA row
+  // lq <- key 32h + 8(lq/4) + 4e + lq%4; its output reg r in lane group g is then
+  // key 32h + 8g + 4e + r, the order ds_read_b64_tr_b16 gives V^T below.
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int rho = 32 * (b >> 1) + 8 * (L.lq >> 2) + 4 * (b & 1) + (L.lq & 3);
+    L.kofs[b][0] = rho * 128 + ((L.g ^ swz_k(rho)) << 4);
+    L.kofs[b][1] = rho * 128 + (((4 + L.g) ^ swz_k(rho)) << 4);
+  }
+  // V^T fragment sources: keys 32h + 8g + lq/4 (+4), dims 16d + 4(lq%4) .. +3.
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int rho = 32 * h + 8 * L.g + (L.lq >> 2) + 4 * s;
+        const int chunk = 2 * d + ((L.lq & 3) >> 1);
+        L.vofs[h][d][s] = kTileBytes + rho * 128 + ((chunk ^ swz_v(rho)) << 4) + 8 * (L.lq & 1);
+      }
+}
+
+// Issue this wave's copies of key tile j of the current item into stage `dst`.
+// Tiles before the diagonal lie wholly inside the user, so their lanes use the
+// fixed offsets from the tile's first row; the diagonal tile clamps rows past the
+// user's end to its last row (finite data under the causal mask, never another
+// user's rows).
+__device__ __forceinline__ void issue_tile(LDS char* dst, const Lanes& L, const uint16_t* kg, const uint16_t* vg,
+                                           int64_t ldq, int j, int len, bool clamp) {
+  LDS char* sk = dst + kRowsPerWave * L.wid * 128;
+  const uint16_t* kt = kg + (int64_t)j * kTileRows * ldq;
+  const uint16_t* vt = vg + (int64_t)j * kTileRows * ldq;
+#pragma unroll
+  for (int i = 0; i < kCopyInstr; ++i) {
+    uint32_t ko = L.kofs_g[i], vo = L.vofs_g[i];
+    if (clamp) {
+      const int r = min(L.crow[i], len - 1 - j * kTileRows);
+      ko = (uint32_t)(r * ldq * 2 + 16 * L.ck[i]);
+      vo = (uint32_t)(r * ldq * 2 + 16 * L.cv[i]);
+    }
+    copy_to_lds(kt, ko, sk + 1024 * i);
+    copy_to_lds(vt, vo, sk + kTileBytes + 1024 * i);
+  }
+}
+
+// Online-softmax state of one lane for each of its query blocks: the running
+// reference max m (raw score units), the O^T accumulator (dims 16d + 4g + r) and
+// the denominator (every register of l holds it).
+struct Acc {
+  float m[kQB];
+  f32x4 o[kQB][4];
+  f32x4 l[kQB];
+};
+
+// One key tile of one item: S^T = K Q^T, mask (diagonal tile only), softmax
+// update, O^T += V^T P^T and l += 1^T P^T, for every query block of the wave.
+template <bool kDiag>
+__device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[kQB][2],
+                                          float sl2, float rescale_thr, Acc& A) {
+  const float NEG_INF = -__builtin_inff();
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  f32x4 s[kQB][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const bf16x8 k0 = lds_b128(base, L.kofs[b][0]);
+    const bf16x8 k1 = lds_b128(base, L.kofs[b][1]);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], s[qb][b], 0, 0, 0);
+    }
+  }
+  if (kDiag) {  // key kk visible to query qr iff kk <= qr
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (32 * (b >> 1) + 8 * L.g + 4 * (b & 1) + r > L.qr[qb]) s[qb][b][r] = NEG_INF;
+  }
+  // Lane-local max over this lane's 16 keys of each query block.  The reference
+  // max m of a query is shared by its 4 lane groups; only when some key exceeds it
+  // by more than the threshold (and on the first tile, m = -inf) is the true row
+  // max formed across the lane groups and m raised, with the accumulators
+  // rescaled.  The common path needs no cross-lane traffic.
+  float lm[kQB];
+  bool raise = false;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    float x = s[qb][0][0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) x = fmaxf(x, s[qb][e >> 2][e & 3]);
+    lm[qb] = x;
+    raise |= x > A.m[qb] + rescale_thr;
+  }
+  if (__any(raise)) {  // wave-uniform
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float mt = max_across_lane_groups(lm[qb]);
+      const float mn = fmaxf(A.m[qb], mt);
+      const float alpha = __builtin_amdgcn_exp2f((A.m[qb] - mn) * sl2);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) A.o[qb][d] *= alpha;
+      A.l[qb] *= alpha;
+      A.m[qb] = mn;
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    // P^T slots 0..7 of lane group g = keys 32hh + 8g + 0..7 = blocks 2hh, 2hh+1
+    bf16x8 pb[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float moff = -A.m[qb] * sl2;
+      const f32x4& s0 = s[qb][2 * hh];
+      const f32x4& s1 = s[qb][2 * hh + 1];
+      uint4 pw;
+      pw.x = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0], sl2, moff)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
+      pw.y = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2], sl2, moff)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(s0[3], sl2, moff)));
+      pw.z = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[0], sl2, moff)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(s1[1], sl2, moff)));
+      pw.w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2], sl2, moff)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(s1[3], sl2, moff)));
+      pb[qb] = __builtin_bit_cast(bf16x8, pw);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bf16x4 lo = lds_tr16(base, L.vofs[hh][d][0]);
+      const bf16x4 hi = lds_tr16(base, L.vofs[hh][d][1]);
+      const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        A.o[qb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb], A.o[qb][d], 0, 0, 0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) A.l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb], A.l[qb], 0, 0, 0);
+  }
+}
 
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                                  const int4* __restrict__ items,
+                                                                 const int32_t* __restrict__ count,
                                                                  int n_heads, float sl2,
                                                                  uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kTileElems];
+  static_assert(kStages == 3, "the tile loop below is unrolled for a 3-stage ring");
+  __shared__ __attribute__((aligned(1024))) Stage ring_lds[kStages];
+  LDS char* const ring0 = (LDS char*)ring_lds[0].bytes;
+  LDS char* const ring1 = (LDS char*)ring_lds[1].bytes;
+  LDS char* const ring2 = (LDS char*)ring_lds[2].bytes;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int g = lane >> 4;   // lane group: k-slot block of the MFMA operands
-  const int lq = lane & 15;  // query column of this lane inside the wave's 16
-  const int qr = wid * 16 + lq;  // query row inside the 64-row tile
   const int64_t ldq = 3 * n_heads * kHeadDim;
+  Lanes L;
+  make_lanes(L, ldq);
   const int64_t ldo = n_heads * kHeadDim;
-  // staging role: 16-byte chunk sc (dims 8sc..8sc+7) of keys 2kp, 2kp+1
-  const int sc = tid & 7;
-  const int kp = tid >> 3;
-  const int vpos = vt_pos(2 * kp);
-  const float NEG_INF = -__builtin_inff();
+  const float rescale_thr = kRescaleLog2 / sl2;  // in raw score units
 
-  for (int w = blockIdx.x;; w += gridDim.x) {
+  const int nwork = *count * n_heads;
+  for (int w = blockIdx.x; w < nwork; w += gridDim.x) {
     const int item = w / n_heads;
     const int h = w - item * n_heads;
     const int4 it = items[item];
-    if (it.x < 0) break;  // sentinel: no more work
     const int qt = it.y;
     const int start = it.z;
     const int len = it.w;
     const int q0 = qt * kTileRows;
-    const bool qvalid = q0 + qr < len;
-    const int64_t qrow = (int64_t)start + q0 + qr;
-
-    bf16x8 qf0, qf1;
-    {
-      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-      if (qvalid) {
-        const uint16_t* p = qkv + qrow * ldq + h * kHeadDim + 8 * g;
-        a = ldg16(p);
-        b = ldg16(p + 32);
-      }
-      qf0 = __builtin_bit_cast(bf16x8, a);
-      qf1 = __builtin_bit_cast(bf16x8, b);
-    }
-    const uint16_t* kg = qkv + (int64_t)start * ldq + n_heads * kHeadDim + h * kHeadDim + 8 * sc;
+    // Items arrive longest first; the longest ones bound the kernel's critical
+    // path, so their waves get issue priority over co-resident shorter items.
+    if (qt >= 32)
+      __builtin_amdgcn_s_setprio(3);
+    else if (qt >= 8)
+      __builtin_amdgcn_s_setprio(2);
+    else if (qt >= 2)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+    const uint16_t* kg = qkv + (int64_t)start * ldq + n_heads * kHeadDim + h * kHeadDim;
     const uint16_t* vg = kg + n_heads * kHeadDim;
 
-    uint4 rk0, rk1, rv0, rv1;
-    auto gload = [&](int j) {
-      const int r = j * kTileRows + 2 * kp;
-      rk0 = rk1 = rv0 = rv1 = make_uint4(0, 0, 0, 0);
-      if (r < len) {
-        rk0 = ldg16(kg + r * ldq);
-        rv0 = ldg16(vg + r * ldq);
+    // The wave's Q rows go through the K half of stage 2: each wave copies and
+    // reads only its own rows, and tile 2 later overwrites exactly those rows of
+    // the same wave, after its Q reads have completed.
+    {
+      LDS char* sq = ring2 + kRowsPerWave * L.wid * 128;
+      const uint16_t* qg = qkv + ((int64_t)start + q0) * ldq + h * kHeadDim;
+#pragma unroll
+      for (int i = 0; i < kCopyInstr; ++i) {
+        const int r = min(L.crow[i], len - 1 - q0);
+        copy_to_lds(qg, (uint32_t)(r * ldq * 2 + 16 * L.ck[i]), sq + 1024 * i);
       }
-      if (r + 1 < len) {
-        rk1 = ldg16(kg + (r + 1) * ldq);
-        rv1 = ldg16(vg + (r + 1) * ldq);
-      }
-    };
-    auto sstore = [&](int buf) {
-      uint16_t* k = sK[buf];
-      *reinterpret_cast<uint4*>(k + (2 * kp) * kLdsRow + 8 * sc) = rk0;
-      *reinterpret_cast<uint4*>(k + (2 * kp + 1) * kLdsRow + 8 * sc) = rk1;
-      // V^T: row = dim, the two keys of this thread side by side.
-      uint32_t* v = reinterpret_cast<uint32_t*>(sV[buf] + (8 * sc) * kLdsRow + vpos);
-      constexpr int rs = kLdsRow / 2;
-      v[0 * rs] = (rv0.x & 0xffffu) | (rv1.x << 16);
-      v[1 * rs] = (rv0.x >> 16) | (rv1.x & 0xffff0000u);
-      v[2 * rs] = (rv0.y & 0xffffu) | (rv1.y << 16);
-      v[3 * rs] = (rv0.y >> 16) | (rv1.y & 0xffff0000u);
-      v[4 * rs] = (rv0.z & 0xffffu) | (rv1.z << 16);
-      v[5 * rs] = (rv0.z >> 16) | (rv1.z & 0xffff0000u);
-      v[6 * rs] = (rv0.w & 0xffffu) | (rv1.w << 16);
-      v[7 * rs] = (rv0.w >> 16) | (rv1.w & 0xffff0000u);
-    };
+    }
+    issue_tile(ring0, L, kg, vg, ldq, 0, len, qt == 0);
+    if (qt >= 1) {
+      issue_tile(ring1, L, kg, vg, ldq, 1, len, qt == 1);
+      wait_vmem_lds<4 * kCopyInstr>();  // this wave's Q rows have landed (tiles 0 and 1 may be in flight)
+    } else {
+      wait_vmem_lds<2 * kCopyInstr>();
+    }
+    bf16x8 qf[kQB][2];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int row = L.qr[qb];
+      qf[qb][0] = lds_b128(ring2, row * 128 + ((L.g ^ swz_k(row)) << 4));
+      qf[qb][1] = lds_b128(ring2, row * 128 + (((4 + L.g) ^ swz_k(row)) << 4));
+    }
+    wait_vmem_lds<4 * kCopyInstr>();  // ... and been read (lgkmcnt), before tile 2 may overwrite them
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    float m = NEG_INF;  // running max of raw scores (this lane's query)
-    float l = 0.f;      // this lane's share of the running denominator
-    f32x4 acc[4];
+    Acc A;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int j = 0; j <= qt; ++j) {
-      const int buf = j & 1;
-      if (j < qt) gload(j + 1);
-
-      // S^T block kb: keys 16kb..16kb+15 of the tile x this wave's 16 queries.
-      const uint16_t* kt = sK[buf] + lq * kLdsRow + 8 * g;
-      f32x4 s[4];
+    for (int qb = 0; qb < kQB; ++qb) {
+      A.m[qb] = -__builtin_inff();
+      A.l[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(kt + 16 * kb * kLdsRow), qf0, s[kb], 0, 0, 0);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(kt + 16 * kb * kLdsRow + 32), qf1, s[kb], 0,
-                                                        0, 0);
-      }
-      if (j == qt) {  // diagonal tile: key kk visible to query qr iff kk <= qr
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (16 * kb + 4 * g + r > qr) s[kb][r] = NEG_INF;
-      }
-      float mt = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f((m - mn) * sl2);
-      const float moff = -mn * sl2;
-      m = mn;
-
-      uint32_t pw[8];  // P^T as bf16 pairs: pw[4*half + 2*blk + i]
-      float ls = 0.f;
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const f32x4& sv = s[2 * half + blk];
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], sl2, moff));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], sl2, moff));
-            const uint32_t wv = pack_bf16x2(p0, p1);
-            pw[4 * half + 2 * blk + i] = wv;
-            ls += bf16lo(wv) + bf16hi(wv);  // denominator from the rounded weights
-          }
-      l = l * alpha + ls;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) acc[d] *= alpha;
-
-      const uint16_t* vt = sV[buf] + lq * kLdsRow + 8 * g;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const uint4 pv = make_uint4(pw[4 * half], pw[4 * half + 1], pw[4 * half + 2], pw[4 * half + 3]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_frag(vt + 16 * d * kLdsRow + 32 * half), pb, acc[d],
-                                                           0, 0, 0);
-      }
-
-      if (j < qt) sstore(buf ^ 1);
-      __syncthreads();
+      for (int d = 0; d < 4; ++d) A.o[qb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = 1.0f / lt;
-    if (qvalid) {
-      uint16_t* o = out + qrow * ldo + h * kHeadDim + 4 * g;
+    // Tile j lives in stage j % 3.  Before consuming it, only the copies of tile
+    // j+1 (if there is one) may still be in flight: wait for the rest, then a
+    // barrier makes every wave's copies visible and frees stage (j+2) % 3.
+    // Off-diagonal tiles (j < qt) run unrolled by the ring size; the diagonal
+    // tile, the only one that needs the causal mask, runs last.
+    for (int j = 0; j < qt; j += 3) {
+      wait_and_barrier<2 * kCopyInstr>();
+      if (j + 2 <= qt) issue_tile(ring2, L, kg, vg, ldq, j + 2, len, j + 2 == qt);
+      tile_step<false>(ring0, L, qf, sl2, rescale_thr, A);
+      if (j + 1 >= qt) break;
+      wait_and_barrier<2 * kCopyInstr>();
+      if (j + 3 <= qt) issue_tile(ring0, L, kg, vg, ldq, j + 3, len, j + 3 == qt);
+      tile_step<false>(ring1, L, qf, sl2, rescale_thr, A);
+      if (j + 2 >= qt) break;
+      wait_and_barrier<2 * kCopyInstr>();
+      if (j + 4 <= qt) issue_tile(ring1, L, kg, vg, ldq, j + 4, len, j + 4 == qt);
+      tile_step<false>(ring2, L, qf, sl2, rescale_thr, A);
+    }
+    wait_and_barrier<0>();
+    const int dst = qt % 3;
+    tile_step<true>(dst == 0 ? ring0 : (dst == 1 ? ring1 : ring2), L, qf, sl2, rescale_thr, A);
+    wait_and_barrier<0>();  // every wave is done with the ring before the next item refills it
+
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint2 wv;
-        wv.x = pack_bf16x2(acc[d][0] * inv, acc[d][1] * inv);
-        wv.y = pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv);
-        *reinterpret_cast<uint2*>(o + 16 * d) = wv;
+    for (int qb = 0; qb < kQB; ++qb) {
+      if (q0 + L.qr[qb] < len) {
+        const float inv = 1.0f / A.l[qb][0];
+        uint16_t* o = out + ((int64_t)start + q0 + L.qr[qb]) * ldo + h * kHeadDim + 4 * L.g;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint2 wv;
+          wv.x = pack_bf16x2(A.o[qb][d][0] * inv, A.o[qb][d][1] * inv);
+          wv.y = pack_bf16x2(A.o[qb][d][2] * inv, A.o[qb][d][3] * inv);
+          *reinterpret_cast<uint2*>(o + 16 * d) = wv;
+        }
       }
     }
   }
@@ -361,10 +562,11 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const void* qkv, const int4* items, int n_heads, float scale_log2e, void* out, int grid,
-                            hipStream_t stream) {
+hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int n_heads,
+                            float scale_log2e, void* out, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(attention_kernel, dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), items, n_heads, scale_log2e, static_cast<uint16_t*>(out));
+                     static_cast<const uint16_t*>(qkv), items, count, n_heads, scale_log2e,
+                     static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
