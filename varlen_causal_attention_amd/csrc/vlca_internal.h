@@ -10,8 +10,13 @@ namespace vlca {
 constexpr int kTileRows = 64;        // query rows per work item == keys per K/V tile
 constexpr int kHeadDim = 64;
 constexpr int kMaxLevels = 4096;     // q-tiles per user the scheduler can order
-constexpr int kStages = 3;           // K/V tile ring depth in LDS (16 KB per stage)
-constexpr int kBlocksPerCU = 3;      // attention workgroups resident per CU (LDS-limited)
+#ifndef VLCA_RING_STAGES
+#define VLCA_RING_STAGES 2
+#endif
+constexpr int kStages = VLCA_RING_STAGES;  // K/V tile ring depth in LDS (16 KB per stage)
+// Attention workgroups resident per CU: 160 KB of LDS shared by rings of
+// kStages * 16 KB, at most 4 (4 waves per SIMD at <= 128 VGPRs).
+constexpr int kBlocksPerCU = (160 / (16 * kStages)) < 4 ? (160 / (16 * kStages)) : 4;
 constexpr int kMaxGrid = 4096;       // persistent grid cap
 
 // Scheduler: one workgroup builds the (user, q_tile, row_start, length) list.

@@ -231,6 +231,33 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
+// Largest number of copies a wave can have in flight behind the one it waits for.
+constexpr int kMaxPending = 2 * kCopyInstr * (kStages - 1);
+
+// Wait until at most n tiles' copies (2*kCopyInstr per wave each) are in flight.
+__device__ __forceinline__ void wait_tiles_pending(int n) {
+  if (n <= 0)
+    wait_vmem_lds<0>();
+  else if (n == 1)
+    wait_vmem_lds<2 * kCopyInstr>();
+  else if (n == 2)
+    wait_vmem_lds<4 * kCopyInstr>();
+  else
+    wait_vmem_lds<6 * kCopyInstr>();
+}
+
+// The same, then the workgroup barrier.
+__device__ __forceinline__ void wait_tiles_pending_barrier(int n) {
+  if (n <= 0)
+    wait_and_barrier<0>();
+  else if (n == 1)
+    wait_and_barrier<2 * kCopyInstr>();
+  else if (n == 2)
+    wait_and_barrier<4 * kCopyInstr>();
+  else
+    wait_and_barrier<6 * kCopyInstr>();
+}
+
 // Copy 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
 // lane l reads base + voff (a wave-uniform 64-bit base, a per-lane 32-bit byte
 // offset) and its bytes land at lds_wave_base + 16*l.  Issued from inline asm so
@@ -442,11 +469,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
                                                                  const int32_t* __restrict__ count,
                                                                  int n_heads, float sl2,
                                                                  uint16_t* __restrict__ out) {
-  static_assert(kStages == 3, "the tile loop below is unrolled for a 3-stage ring");
+  static_assert(kStages >= 2 && kStages <= 4, "ring depth");
   __shared__ __attribute__((aligned(1024))) Stage ring_lds[kStages];
-  LDS char* const ring0 = (LDS char*)ring_lds[0].bytes;
-  LDS char* const ring1 = (LDS char*)ring_lds[1].bytes;
-  LDS char* const ring2 = (LDS char*)ring_lds[2].bytes;
+  LDS char* const ring = (LDS char*)ring_lds[0].bytes;
+  auto stage = [&](int j) { return ring + (j % kStages) * kStageBytes; };
 
   const int64_t ldq = 3 * n_heads * kHeadDim;
   Lanes L;
@@ -476,11 +502,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     const uint16_t* kg = qkv + (int64_t)start * ldq + n_heads * kHeadDim + h * kHeadDim;
     const uint16_t* vg = kg + n_heads * kHeadDim;
 
-    // The wave's Q rows go through the K half of stage 2: each wave copies and
-    // reads only its own rows, and tile 2 later overwrites exactly those rows of
-    // the same wave, after its Q reads have completed.
+    // The wave's Q rows go through the K half of the last ring stage: each wave
+    // copies and reads only its own rows, and tile kStages-1 later overwrites
+    // exactly those rows of the same wave, after its Q reads have completed.
+    LDS char* const qstage = ring + (kStages - 1) * kStageBytes;
     {
-      LDS char* sq = ring2 + kRowsPerWave * L.wid * 128;
+      LDS char* sq = qstage + kRowsPerWave * L.wid * 128;
       const uint16_t* qg = qkv + ((int64_t)start + q0) * ldq + h * kHeadDim;
 #pragma unroll
       for (int i = 0; i < kCopyInstr; ++i) {
@@ -488,21 +515,20 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
         copy_to_lds(qg, (uint32_t)(r * ldq * 2 + 16 * L.ck[i]), sq + 1024 * i);
       }
     }
-    issue_tile(ring0, L, kg, vg, ldq, 0, len, qt == 0);
-    if (qt >= 1) {
-      issue_tile(ring1, L, kg, vg, ldq, 1, len, qt == 1);
-      wait_vmem_lds<4 * kCopyInstr>();  // this wave's Q rows have landed (tiles 0 and 1 may be in flight)
-    } else {
-      wait_vmem_lds<2 * kCopyInstr>();
-    }
+    // Prologue: tiles 0 .. kStages-2 (those that exist) into stages 0 .. kStages-2.
+    const int pre = min(qt, kStages - 2);  // index of the last prologue tile
+#pragma unroll
+    for (int j = 0; j <= kStages - 2; ++j)
+      if (j <= pre) issue_tile(ring + j * kStageBytes, L, kg, vg, ldq, j, len, j == qt);
+    wait_tiles_pending(pre + 1);  // this wave's Q rows have landed (all prologue tiles may be in flight)
     bf16x8 qf[kQB][2];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const int row = L.qr[qb];
-      qf[qb][0] = lds_b128(ring2, row * 128 + ((L.g ^ swz_k(row)) << 4));
-      qf[qb][1] = lds_b128(ring2, row * 128 + (((4 + L.g) ^ swz_k(row)) << 4));
+      qf[qb][0] = lds_b128(qstage, row * 128 + ((L.g ^ swz_k(row)) << 4));
+      qf[qb][1] = lds_b128(qstage, row * 128 + (((4 + L.g) ^ swz_k(row)) << 4));
     }
-    wait_vmem_lds<4 * kCopyInstr>();  // ... and been read (lgkmcnt), before tile 2 may overwrite them
+    wait_vmem_lds<kMaxPending>();  // ... and been read (lgkmcnt) before that stage is refilled
 
     Acc A;
 #pragma unroll
@@ -513,27 +539,19 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       for (int d = 0; d < 4; ++d) A.o[qb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Tile j lives in stage j % 3.  Before consuming it, only the copies of tile
-    // j+1 (if there is one) may still be in flight: wait for the rest, then a
-    // barrier makes every wave's copies visible and frees stage (j+2) % 3.
-    // Off-diagonal tiles (j < qt) run unrolled by the ring size; the diagonal
-    // tile, the only one that needs the causal mask, runs last.
-    for (int j = 0; j < qt; j += 3) {
-      wait_and_barrier<2 * kCopyInstr>();
-      if (j + 2 <= qt) issue_tile(ring2, L, kg, vg, ldq, j + 2, len, j + 2 == qt);
-      tile_step<false>(ring0, L, qf, sl2, rescale_thr, A);
-      if (j + 1 >= qt) break;
-      wait_and_barrier<2 * kCopyInstr>();
-      if (j + 3 <= qt) issue_tile(ring0, L, kg, vg, ldq, j + 3, len, j + 3 == qt);
-      tile_step<false>(ring1, L, qf, sl2, rescale_thr, A);
-      if (j + 2 >= qt) break;
-      wait_and_barrier<2 * kCopyInstr>();
-      if (j + 4 <= qt) issue_tile(ring1, L, kg, vg, ldq, j + 4, len, j + 4 == qt);
-      tile_step<false>(ring2, L, qf, sl2, rescale_thr, A);
+    // Tile j lives in stage j % kStages.  Before consuming it, only the copies of
+    // tiles j+1 .. j+kStages-2 (those that exist) may still be in flight: wait
+    // for the rest, then a barrier makes every wave's copies visible and frees
+    // stage (j-1) % kStages for tile j+kStages-1.  Off-diagonal tiles (j < qt)
+    // need no mask; the diagonal tile runs last.
+    for (int j = 0; j < qt; ++j) {
+      wait_tiles_pending_barrier(min(qt - j, kStages - 2));
+      if (j + kStages - 1 <= qt) issue_tile(stage(j + kStages - 1), L, kg, vg, ldq, j + kStages - 1, len,
+                                            j + kStages - 1 == qt);
+      tile_step<false>(stage(j), L, qf, sl2, rescale_thr, A);
     }
     wait_and_barrier<0>();
-    const int dst = qt % 3;
-    tile_step<true>(dst == 0 ? ring0 : (dst == 1 ? ring1 : ring2), L, qf, sl2, rescale_thr, A);
+    tile_step<true>(stage(qt), L, qf, sl2, rescale_thr, A);
     wait_and_barrier<0>();  // every wave is done with the ring before the next item refills it
 
 #pragma unroll
