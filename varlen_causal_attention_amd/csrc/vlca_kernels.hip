@@ -480,22 +480,41 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   const int64_t ldo = n_heads * kHeadDim;
   const float rescale_thr = kRescaleLog2 / sl2;  // in raw score units
 
-  const int nwork = *count * n_heads;
-  for (int w = blockIdx.x; w < nwork; w += gridDim.x) {
-    const int item = w / n_heads;
-    const int h = w - item * n_heads;
+  // Work assignment.  With the grid a multiple of H, workgroup g always runs head
+  // g % H (with H = 8 that is the XCD it sits on) and item slot g / H of each
+  // round; rounds alternate direction (snake), so the workgroups that drew the
+  // longest items of round 0 draw the shortest of round 1.
+  const int nitems = *count;
+  const int G = gridDim.x;
+  const bool by_head = G % n_heads == 0;
+  const int slots = by_head ? G / n_heads : G;
+  const int slot = by_head ? blockIdx.x / n_heads : blockIdx.x;
+  const int head0 = by_head ? blockIdx.x - slot * n_heads : 0;
+  const int qt_max = nitems > 0 ? items[0].y : 0;  // items arrive longest first
+  for (int round = 0;; ++round) {
+    const int pos = (round & 1) ? slots - 1 - slot : slot;
+    int item, h;
+    if (by_head) {
+      item = round * slots + pos;
+      h = head0;
+    } else {
+      const int w = round * slots + pos;
+      item = w / n_heads;
+      h = w - item * n_heads;
+    }
+    if (item >= nitems) break;
     const int4 it = items[item];
     const int qt = it.y;
     const int start = it.z;
     const int len = it.w;
     const int q0 = qt * kTileRows;
-    // Items arrive longest first; the longest ones bound the kernel's critical
-    // path, so their waves get issue priority over co-resident shorter items.
-    if (qt >= 32)
+    // The longest items bound the kernel's critical path: their waves get issue
+    // priority over co-resident shorter items.
+    if (qt >= 1 && 2 * qt >= qt_max)
       __builtin_amdgcn_s_setprio(3);
-    else if (qt >= 8)
+    else if (qt >= 1 && 4 * qt >= qt_max)
       __builtin_amdgcn_s_setprio(2);
-    else if (qt >= 2)
+    else if (qt >= 1)
       __builtin_amdgcn_s_setprio(1);
     else
       __builtin_amdgcn_s_setprio(0);
