@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -85,6 +86,117 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {r}/gpurun_out/prof/trace -o run -- "
+             "python3 {r}/bench.py --config {c} --steps 200 --warmup 20 --no-cpu-baseline --cold-steps 0",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {r}/gpurun_out/prof/fetch -o run -- "
+             "python3 {r}/bench.py --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {r}/gpurun_out/prof/write -o run -- "
+             "python3 {r}/bench.py --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
+    "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {r}/gpurun_out/prof/copyf -o run -- "
+             "python3 {r}/bench.py --calibrate-copy-mib 256 --steps 5",
+    "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {r}/gpurun_out/prof/copyw -o run -- "
+             "python3 {r}/bench.py --calibrate-copy-mib 256 --steps 5",
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _read_csv(path):
+    import csv
+
+    with open(path, newline="", encoding="utf-8") as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_mean(d: str, kernel_substr: str, counter: str):
+    rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv"))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    vals = [float(r["Counter_Value"]) for r in rows]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} under {d}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_profiles(root: str, config: int) -> None:
+    """Write profiles/attention_kernel_<workload>_{trace,pmc}.txt from rocprofv3 CSV output.
+
+    ``root`` holds one folder per rocprofv3 run (commands in PROFILE_COMMANDS, with
+    $REPO the repository root, run from /tmp with TMPDIR=/tmp), plus
+    ``kernel_sha.txt`` (sha256 of the kernel source the runs used) and, optionally,
+    ``trace.log`` (that run's stdout/stderr with the bench line).
+    """
+    import workloads
+
+    w = workloads.make_config(config, with_values=False)
+    sha_path = os.path.join(root, "kernel_sha.txt")
+    sha = open(sha_path, encoding="utf-8").read().split()[0][:16] if os.path.exists(sha_path) else "unknown"
+    if sha != kernel_source_hash():
+        print(f"warning: profiles were taken on kernel source {sha}, tree has {kernel_source_hash()}",
+              file=sys.stderr)
+    cmds = {k: "cd /tmp && export TMPDIR=/tmp && " + v.format(r="$REPO", c=config)
+            for k, v in PROFILE_COMMANDS.items()}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+
+    # Kernel trace: per-kernel duration statistics.
+    stats = _read_csv(os.path.join(root, "trace", "run_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel trace, workload {w.name} ({w.total_tokens} tokens, {w.num_users} users)",
+             f"# command: {cmds['trace']}",
+             f"kernel_source_sha256_16: {sha}",
+             "",
+             f"{'kernel':<28} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    for r in stats:
+        m = re.search(r"([A-Za-z_]\w*)\(", r["Name"])
+        short = m.group(1) if m else r["Name"][:28]
+        lines.append(f"{short:<28} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.3f} "
+                     f"{float(r['MinNs']) / 1e3:>9.3f} {float(r['MaxNs']) / 1e3:>9.3f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    log = os.path.join(root, "trace.log")
+    if os.path.exists(log):
+        bench_lines = [ln for ln in open(log, encoding="utf-8") if ln.startswith("[bench]") or ln.startswith("{")]
+        if bench_lines:
+            lines += ["", "# the profiled bench run printed (its event timings include profiler overhead):"]
+            lines += ["#   " + ln.rstrip()[:400] for ln in bench_lines]
+    with open(os.path.join(ROOT, "profiles", f"attention_kernel_{w.name}_trace.txt"), "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM traffic: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy's reading.
+    fetch_kib, n_f = _counter_mean(os.path.join(root, "fetch"), ATTN_KERNEL, "FETCH_SIZE")
+    write_kib, n_w = _counter_mean(os.path.join(root, "write"), ATTN_KERNEL, "WRITE_SIZE")
+    copy_f, _ = _counter_mean(os.path.join(root, "copyf"), COPY_KERNEL, "FETCH_SIZE")
+    copy_w, _ = _counter_mean(os.path.join(root, "copyw"), COPY_KERNEL, "WRITE_SIZE")
+    copy_bytes = 256 * 2**20
+    f_factor = copy_bytes / (copy_f * 1024.0)
+    w_factor = copy_bytes / (copy_w * 1024.0)
+    rd = fetch_kib * 1024.0 * f_factor
+    wr = write_kib * 1024.0 * w_factor
+    lines = [f"# rocprofv3 HBM counters for {ATTN_KERNEL}, workload {w.name}",
+             f"# command (fetch): {cmds['fetch']}",
+             f"# command (write): {cmds['write']}",
+             f"# command (copy calibration, fetch): {cmds['copyf']}",
+             f"# command (copy calibration, write): {cmds['copyw']}",
+             "# FETCH_SIZE/WRITE_SIZE are KiB per dispatch; each is scaled by what it reads for a",
+             "# 256 MiB device-to-device copy (known bytes), averaged over the dispatches listed.",
+             f"kernel_source_sha256_16: {sha}",
+             f"workload: {w.name}",
+             f"fetch_kib_per_dispatch: {fetch_kib:.3f}",
+             f"fetch_dispatches: {n_f}",
+             f"write_kib_per_dispatch: {write_kib:.3f}",
+             f"write_dispatches: {n_w}",
+             f"copy_bytes: {copy_bytes}",
+             f"copy_fetch_kib: {copy_f:.3f}",
+             f"copy_write_kib: {copy_w:.3f}",
+             f"fetch_scale: {f_factor:.4f}",
+             f"write_scale: {w_factor:.4f}",
+             f"hbm_read_bytes_per_launch: {rd:.0f}",
+             f"hbm_write_bytes_per_launch: {wr:.0f}",
+             f"hbm_bytes_per_launch: {rd + wr:.0f}",
+             f"algorithmic_bytes_per_launch: {w.algorithmic_bytes()}",
+             f"traffic_over_algorithmic: {(rd + wr) / w.algorithmic_bytes():.4f}"]
+    with open(os.path.join(ROOT, "profiles", f"attention_kernel_{w.name}_pmc.txt"), "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,7 +207,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB --steps times (HBM counter calibration)")
+    ap.add_argument("--cold-steps", type=int, default=30,
+                    help="single launches timed after a 512 MiB scratch write (cache-cold step time)")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="no GPU: turn the rocprofv3 CSV output under DIR (trace/, fetch/, write/, copyf/, "
+                         "copyw/) into the text summaries under profiles/")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.config)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -163,6 +284,22 @@ def main():
     print(f"[bench] step {ms_step * 1e3:.2f} us, attention kernel {ms_attn * 1e3:.2f} us",
           file=sys.stderr, flush=True)
 
+    # Cache-cold step: a 512 MiB write evicts L2 and the 256 MiB MALL before each
+    # single timed step.
+    cold_ms = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(args.cold_steps):
+            scratch.fill_(1)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del scratch
+        cold_ms = sorted(cold)[len(cold) // 2]
+
     flops = w.causal_flops()
     nbytes = w.algorithmic_bytes()
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -196,6 +333,7 @@ def main():
             "qkv": f"bf16 [{w.total_tokens}, {3 * w.n_heads * w.head_dim}]",
             "length_law": "lognormal(4.3, 0.9) rescaled, seed 0" if args.config == 2 else "see workloads.py",
         },
+        "cold_ms_per_step": cold_ms,
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "causal_gflop": flops / 1e9,
