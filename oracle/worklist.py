@@ -11,13 +11,15 @@ a compact list that holds exactly the (user, q-tile) pairs that have rows:
 
 * user ``u`` with length ``L`` owns ``ceil(L / tile_rows)`` q-tiles; zero-length
   users own none;
-* q-tile ``k`` of a user needs ``k + 1`` key tiles (it stops at the diagonal), so
-  items are emitted longest first: for ``k`` from the largest tile index down to
-  0, every user that has a tile ``k``, in ascending user order.
+* q-tile ``k`` of a user needs ``k + 1`` key tiles (it stops at the diagonal).
 
-The order is a design choice of this library (longest-processing-time first
-for the persistent kernel); the list is unique under it, so the GPU-built list
-must match this one element for element.
+Order (a design choice of this library, not of the pages).  Users are grouped
+by length class ``floor(log2(tiles))``, longest class first, so the longest
+users' work starts first; inside a class users ascend; each user's q-tiles are
+listed together, from the last one (the most key tiles) down to q-tile 0.
+Keeping a user's q-tiles adjacent makes the work items that run at the same
+time share that user's key/value rows.  The list is unique under this rule,
+so the GPU-built list must match this one element for element.
 """
 from __future__ import annotations
 
@@ -35,13 +37,23 @@ def tiles_per_user(cu_seqlens, tile_rows: int, max_tiles: int | None = None) -> 
     return nt
 
 
+def length_class(tiles: int) -> int:
+    """floor(log2(tiles)) for tiles >= 1."""
+    c = 0
+    while (2 << c) <= tiles:
+        c += 1
+    return c
+
+
 def reference_worklist(cu_seqlens, tile_rows: int, max_tiles: int | None = None) -> np.ndarray:
     """int32 ``[N, 2]`` array of (user, q_tile) in the scheduler's order, by plain loops."""
     nt = tiles_per_user(cu_seqlens, tile_rows, max_tiles)
     items = []
-    top = int(nt.max()) if nt.size else 0
-    for k in range(top - 1, -1, -1):
-        for u in range(nt.shape[0]):
-            if nt[u] > k:
-                items.append((u, k))
+    users = [u for u in range(nt.shape[0]) if nt[u] > 0]
+    top = max((length_class(int(nt[u])) for u in users), default=-1)
+    for c in range(top, -1, -1):
+        for u in users:
+            if length_class(int(nt[u])) == c:
+                for k in range(int(nt[u]) - 1, -1, -1):
+                    items.append((u, k))
     return np.asarray(items, dtype=np.int32).reshape(-1, 2)

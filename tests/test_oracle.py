@@ -233,9 +233,11 @@ def test_worklist_equals_sorted_pairs(seed):
     lengths = rng.integers(0, 300, rng.integers(1, 40))
     cu = workloads.cu_from_lengths(lengths)
     got = oracle.reference_worklist(cu, 64)
-    # Independent formulation: all (u, k) pairs, sorted by (-k, u).
-    pairs = [(u, k) for u, L in enumerate(lengths) for k in range(-(-int(L) // 64))]
-    pairs.sort(key=lambda p: (-p[1], p[0]))
+    # Independent formulation: all (u, k) pairs, sorted by (-class, u, -k) with the
+    # length class floor(log2(tiles)) taken from the bit length of the tile count.
+    tiles = [-(-int(L) // 64) for L in lengths]
+    pairs = [(u, k) for u, t in enumerate(tiles) for k in range(t)]
+    pairs.sort(key=lambda p: (-(tiles[p[0]].bit_length() - 1), p[0], -p[1]))
     np.testing.assert_array_equal(got, np.array(pairs, dtype=np.int32).reshape(-1, 2))
     assert got.shape[0] == int(np.sum((lengths + 63) // 64))
 
@@ -252,6 +254,16 @@ def test_worklist_max_tiles_clamp():
     cu = workloads.cu_from_lengths([300, 10])
     got = oracle.reference_worklist(cu, 64, max_tiles=2)
     np.testing.assert_array_equal(got, [[0, 1], [0, 0], [1, 0]])
+
+
+def test_worklist_length_classes():
+    # Tiles 1, 2, 3, 4, 7, 8 -> classes 0, 1, 1, 2, 2, 3: user 5 first, then users
+    # 3 and 4 (class 2, ascending), then 1 and 2, then 0; q-tiles descending.
+    cu = workloads.cu_from_lengths([64, 128, 192, 256, 448, 512])
+    got = oracle.reference_worklist(cu, 64)
+    want = [(5, k) for k in range(7, -1, -1)] + [(3, k) for k in range(3, -1, -1)] + \
+        [(4, k) for k in range(6, -1, -1)] + [(1, 1), (1, 0), (2, 2), (2, 1), (2, 0), (0, 0)]
+    np.testing.assert_array_equal(got, np.array(want, dtype=np.int32))
 
 
 def test_row_sampled_oracle_matches_full():
