@@ -24,7 +24,7 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
-std::map<int, int> g_cu_count;
+std::map<int, int> g_resident;  // device -> resident attention workgroups
 
 int64_t max_tiles_of(int max_seqlen) { return (static_cast<int64_t>(max_seqlen) + vlca::kTileRows - 1) / vlca::kTileRows; }
 
@@ -52,18 +52,20 @@ int check_attention_args(const void* qkv, const int32_t* cu_seqlens, int num_use
   return VLCA_OK;
 }
 
-int cu_count(int dev) {
+// Resident attention workgroups per device: CUs x workgroups per CU.
+int resident_blocks(int dev) {
   std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_cu_count.find(dev);
-  if (it != g_cu_count.end()) return it->second;
+  auto it = g_resident.find(dev);
+  if (it != g_resident.end()) return it->second;
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  g_cu_count[dev] = n;
-  return n;
+  const int r = n * vlca::attention_blocks_per_cu();
+  g_resident[dev] = r;
+  return r;
 }
 
 int grid_size(int dev, int num_users, int max_seqlen, int n_heads) {
-  int64_t g = static_cast<int64_t>(cu_count(dev)) * vlca::kBlocksPerCU;
+  int64_t g = resident_blocks(dev);
   if (g > vlca::kMaxGrid) g = vlca::kMaxGrid;
   g -= g % 8;  // keeps w % 8 == blockIdx.x % 8 (one head per XCD when H = 8)
   if (g < 8) g = 8;

@@ -10,13 +10,6 @@ namespace vlca {
 constexpr int kTileRows = 64;        // query rows per work item == keys per K/V tile
 constexpr int kHeadDim = 64;
 constexpr int kMaxLevels = 4096;     // q-tiles per user the scheduler can order
-#ifndef VLCA_RING_STAGES
-#define VLCA_RING_STAGES 2
-#endif
-constexpr int kStages = VLCA_RING_STAGES;  // K/V tile ring depth in LDS (16 KB per stage)
-// Attention workgroups resident per CU: 160 KB of LDS shared by rings of
-// kStages * 16 KB, at most 4 (4 waves per SIMD at <= 128 VGPRs).
-constexpr int kBlocksPerCU = (160 / (16 * kStages)) < 4 ? (160 / (16 * kStages)) : 4;
 constexpr int kMaxGrid = 4096;       // persistent grid cap
 
 // Scheduler: one workgroup builds the (user, q_tile, row_start, length) list.
@@ -26,5 +19,8 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 // Attention: persistent grid walking the first *count items (heads fastest).
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int n_heads,
                             float scale_log2e, void* out, int grid, hipStream_t stream);
+
+// Attention workgroups that fit on one CU at once (occupancy of the current device).
+int attention_blocks_per_cu();
 
 }  // namespace vlca

@@ -56,14 +56,8 @@ typedef LDS bf16x4 lds_bf16x4;
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedCache = 8160;  // cu_seqlens entries cached in LDS by the scheduler (LDS <= 64 KB)
-#ifndef VLCA_QUERY_BLOCKS_PER_WAVE
-#define VLCA_QUERY_BLOCKS_PER_WAVE 1
-#endif
-constexpr int kQB = VLCA_QUERY_BLOCKS_PER_WAVE;        // 16-row query blocks per wave (1, 2 or 4)
-constexpr int kRowsPerWave = 16 * kQB;
-constexpr int kWaves = kTileRows / kRowsPerWave;       // waves per workgroup
+constexpr int kWaves = 4;                              // wave w owns query rows 16w .. 16w+15
 constexpr int kAttnThreads = 64 * kWaves;
-constexpr int kCopyInstr = kRowsPerWave / 8;           // 1 KB copy instructions per wave per 8 KB tile
 constexpr int kTileBytes = kTileRows * kHeadDim * 2;  // 8 KB: one 64 x 64 bf16 tile, 128 B rows
 constexpr int kStageBytes = 2 * kTileBytes;           // K tile then V tile
 constexpr float kRescaleLog2 = 8.0f;
@@ -88,35 +82,38 @@ __device__ __forceinline__ Seg segment_of(const int32_t* __restrict__ cu, const 
   return s;
 }
 
-// out[k] = sum_{j > k} a[j] for k < n (in place, one wave); returns the total.
-__device__ int wave_suffix_exclusive(int* a, int n, int lane) {
-  const int chunk = (n + 63) / 64;
-  const int lo = lane * chunk;
-  const int hi = min(lo + chunk, n);
-  int local = 0;
-  for (int k = lo; k < hi; ++k) local += a[k];
-  int incl = local;  // inclusive suffix over lanes >= lane
+// Length class of a user with t >= 1 tiles: floor(log2(t)).
+__device__ __forceinline__ int length_class(int t) { return 31 - __builtin_clz((unsigned)t); }
+
+__device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
+#pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_down(incl, off);
-    if (lane + off < 64) incl += t;
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  int run = incl - local;
-  for (int k = hi - 1; k >= lo; --k) {
-    const int v = a[k];
-    a[k] = run;
-    run += v;
-  }
-  return __shfl(incl, 0);
+  return x;
 }
 
+constexpr int kClasses = 13;       // tile counts up to kMaxLevels = 4096 -> classes 0..12
+constexpr int kShortTiles = 16;    // users with more tiles are emitted by a whole wave
+
+// Worklist order: users grouped by length class, highest class first; inside a
+// class users ascend; each user's q-tiles are adjacent, from its last q-tile
+// (the most key tiles) down to q-tile 0.  The first slot of user u is then
+//   sum of the tiles of all higher classes + sum of the tiles of the users
+//   before u in its own class,
+// computed in two passes over the users (class totals, then per-class running
+// sums in chunks of kSchedThreads users).
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ cu, int U,
                                                                  int max_tiles, int4* __restrict__ items,
                                                                  int32_t* __restrict__ count) {
   __shared__ int s_cu[kSchedCache + 1];
-  __shared__ int s_cnt[kMaxLevels + 1];  // histogram of tile counts, then users per level
-  __shared__ int s_pos[kMaxLevels + 1];  // first worklist slot of each level
-  __shared__ int s_wmax[kSchedThreads / 64];
-  __shared__ int s_total;
+  __shared__ int s_tot[kClasses];                     // tiles per class
+  __shared__ int s_base[kClasses];                    // next free slot of each class
+  __shared__ int s_wsum[kSchedThreads / 64][kClasses];  // per-wave class sums of the current chunk
+  __shared__ int s_long[kSchedThreads];               // long users of the current chunk ...
+  __shared__ int s_longoff[kSchedThreads];            // ... and their first slots
+  __shared__ int s_nlong;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,56 +122,74 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   if (U > 0 && max_tiles > 0 && cached) {
     for (int i = tid; i <= U; i += kSchedThreads) s_cu[i] = cu[i];
   }
+  if (tid < kClasses) s_tot[tid] = 0;
   __syncthreads();
   const int total = (U > 0 && max_tiles > 0) ? (cached ? s_cu[U] : cu[U]) : 0;
   const int nusers = max_tiles > 0 ? U : 0;
 
-  // Largest tile count over users.
-  int tmax = 0;
-  for (int u = tid; u < nusers; u += kSchedThreads)
-    tmax = max(tmax, segment_of(cu, s_cu, cached, u, total, max_tiles).tiles);
-  for (int off = 32; off > 0; off >>= 1) tmax = max(tmax, __shfl_xor(tmax, off));
-  if (lane == 0) s_wmax[wid] = tmax;
-  for (int k = tid; k <= kMaxLevels; k += kSchedThreads) s_cnt[k] = 0;
-  __syncthreads();
-  int levels = 0;
-  for (int i = 0; i < kSchedThreads / 64; ++i) levels = max(levels, s_wmax[i]);
-
+  // Pass 1: tiles per class.
   for (int u = tid; u < nusers; u += kSchedThreads) {
     const int t = segment_of(cu, s_cu, cached, u, total, max_tiles).tiles;
-    if (t > 0) atomicAdd(&s_cnt[t], 1);
+    if (t > 0) atomicAdd(&s_tot[length_class(t)], t);
   }
   __syncthreads();
-  // users with more than k tiles: c[k] = sum_{t > k} hist[t]
-  if (wid == 0) wave_suffix_exclusive(s_cnt, levels + 1, lane);
-  __syncthreads();
-  for (int k = tid; k < levels; k += kSchedThreads) s_pos[k] = s_cnt[k];
-  __syncthreads();
-  // first slot of level k: the items of all higher levels come first
-  if (wid == 0) {
-    const int n = wave_suffix_exclusive(s_pos, levels, lane);
-    if (lane == 0) s_total = n;
-  }
-  __syncthreads();
-
-  // Each wave emits whole levels; inside a level users ascend (ballot compaction).
-  for (int k = wid; k < levels; k += kSchedThreads / 64) {
-    int slot = s_pos[k];
-    const int end = slot + s_cnt[k];
-    for (int base = 0; base < nusers && slot < end; base += 64) {
-      const int u = base + lane;
-      Seg s{0, 0, 0};
-      if (u < nusers) s = segment_of(cu, s_cu, cached, u, total, max_tiles);
-      const bool take = s.tiles > k;
-      const unsigned long long m = __ballot(take);
-      if (take) {
-        const int rank = __popcll(m & ((1ull << lane) - 1ull));
-        items[slot + rank] = make_int4(u, k, s.start, s.len);
-      }
-      slot += __popcll(m);
+  if (tid == 0) {
+    int run = 0;
+    for (int c = kClasses - 1; c >= 0; --c) {
+      s_base[c] = run;
+      run += s_tot[c];
     }
+    *count = run;
   }
-  if (tid == 0) *count = s_total;
+
+  // Pass 2: slots, chunk by chunk in ascending user order.
+  for (int c0 = 0; c0 < nusers; c0 += kSchedThreads) {
+    if (tid == 0) s_nlong = 0;
+    if (lane < kClasses) s_wsum[wid][lane] = 0;
+    const int u = c0 + tid;
+    Seg s{0, 0, 0};
+    if (u < nusers) s = segment_of(cu, s_cu, cached, u, total, max_tiles);
+    const int t = s.tiles;
+    const int cl = t > 0 ? length_class(t) : -1;
+    // Exclusive prefix of the tile counts of earlier lanes in the same class, one
+    // wave scan per class present in the wave.
+    int pre = 0;
+    unsigned long long pending = __ballot(t > 0);
+    while (pending) {
+      const int lc = __shfl(cl, __builtin_ctzll(pending));
+      const bool mine = cl == lc;
+      const int x = mine ? t : 0;
+      const int incl = wave_inclusive_sum(x, lane);
+      if (mine) pre = incl - x;
+      if (lane == 63) s_wsum[wid][lc] = incl;
+      pending &= ~__ballot(mine);
+    }
+    __syncthreads();
+    if (t > 0) {
+      int off = s_base[cl] + pre;
+      for (int w = 0; w < wid; ++w) off += s_wsum[w][cl];
+      if (t <= kShortTiles) {
+        for (int i = 0; i < t; ++i) items[off + i] = make_int4(u, t - 1 - i, s.start, s.len);
+      } else {
+        const int k = atomicAdd(&s_nlong, 1);
+        s_long[k] = u;
+        s_longoff[k] = off;
+      }
+    }
+    __syncthreads();
+    for (int i = wid; i < s_nlong; i += kSchedThreads / 64) {
+      const int lu = s_long[i];
+      const int off = s_longoff[i];
+      const Seg ls = segment_of(cu, s_cu, cached, lu, total, max_tiles);
+      for (int k = lane; k < ls.tiles; k += 64) items[off + k] = make_int4(lu, ls.tiles - 1 - k, ls.start, ls.len);
+    }
+    if (tid < kClasses) {
+      int sum = 0;
+      for (int w = 0; w < kSchedThreads / 64; ++w) sum += s_wsum[w][tid];
+      s_base[tid] += sum;
+    }
+    __syncthreads();
+  }
 }
 
 // ----------------------------------------------------------------- attention
@@ -186,10 +201,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
 __device__ __forceinline__ int swz_k(int r) { return ((r & 3) ^ ((r >> 4) & 1)) | (((r >> 3) & 1) << 2); }
 __device__ __forceinline__ int swz_v(int r) { return ((r & 3) ^ ((r >> 3) & 1)) << 1; }
 
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// LDS reads go through address-space-3 pointers derived from the stage object
-// itself, so the compiler can see which copies they may depend on.
 __device__ __forceinline__ bf16x8 lds_b128(const LDS char* base, int byte_off) {
   return __builtin_bit_cast(bf16x8, *(const LDS u32x4*)(base + byte_off));
 }
@@ -208,6 +219,9 @@ __device__ __forceinline__ float max_across_lane_groups(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// NaN-propagating maximum (v_maximum3_f32 on gfx950; no canonicalising moves).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // RNE
@@ -223,53 +237,25 @@ __device__ __forceinline__ void wait_vmem_lds() {
 }
 
 // The same wait followed by a workgroup barrier.  __syncthreads() would add a
-// release fence that also waits for every LDS copy still in flight, draining the
-// tile ring; here only what the caller names (n copies may stay in flight).
+// release fence that also waits for every LDS copy still in flight; here only
+// what the caller names (n copies may stay in flight).
 template <int n>
 __device__ __forceinline__ void wait_and_barrier() {
   static_assert(n >= 0 && n < 64, "vmcnt immediate");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
-// Largest number of copies a wave can have in flight behind the one it waits for.
-constexpr int kMaxPending = 2 * kCopyInstr * (kStages - 1);
-
-// Wait until at most n tiles' copies (2*kCopyInstr per wave each) are in flight.
-__device__ __forceinline__ void wait_tiles_pending(int n) {
-  if (n <= 0)
-    wait_vmem_lds<0>();
-  else if (n == 1)
-    wait_vmem_lds<2 * kCopyInstr>();
-  else if (n == 2)
-    wait_vmem_lds<4 * kCopyInstr>();
-  else
-    wait_vmem_lds<6 * kCopyInstr>();
-}
-
-// The same, then the workgroup barrier.
-__device__ __forceinline__ void wait_tiles_pending_barrier(int n) {
-  if (n <= 0)
-    wait_and_barrier<0>();
-  else if (n == 1)
-    wait_and_barrier<2 * kCopyInstr>();
-  else if (n == 2)
-    wait_and_barrier<4 * kCopyInstr>();
-  else
-    wait_and_barrier<6 * kCopyInstr>();
-}
-
 // Copy 16 bytes per lane from global memory into LDS (global_load_lds_dwordx4):
 // lane l reads base + voff (a wave-uniform 64-bit base, a per-lane 32-bit byte
-// offset) and its bytes land at lds_wave_base + 16*l.  Issued from inline asm so
-// that the compiler, which would otherwise track these LDS writes coarsely and
-// insert waits for every copy in flight before unrelated LDS reads, leaves all
-// waits on them to the explicit wait_vmem_lds / wait_and_barrier calls.  The
-// instruction has no register result; M0 (the LDS base operand) is saved and
-// restored around it.
-__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, const LDS void* lds_wave_base) {
+// offset) and its bytes land at LDS address m + 16*l (m wave-uniform).  Issued
+// from inline asm so that the compiler, which would otherwise track these LDS
+// writes coarsely and insert waits for every copy in flight before unrelated LDS
+// reads, leaves all waits on them to the explicit wait_vmem_lds /
+// wait_and_barrier calls.  The instruction has no register result; M0 (the LDS
+// base operand) is saved and restored around it.
+__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, uint32_t m) {
   // readfirstlane returns int: widen through uint32_t so the low word is not
   // sign-extended into the high word of the 64-bit base.
-  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
   const uint64_t sbase = (uint64_t)lo | ((uint64_t)hi << 32);
@@ -285,22 +271,17 @@ __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, con
       : "memory");
 }
 
-// One ring stage: the K tile then the V tile.
-struct Stage {
-  char bytes[kStageBytes];
-};
-
 // Per-lane constants of the attention workgroup.  Wave w owns query rows
-// kRowsPerWave*w .. kRowsPerWave*(w+1)-1 of the 64-row tile, as kQB blocks of 16;
-// it also copies those rows of every K, V and Q tile into LDS.
+// 16w .. 16w+15 of the tile; it also copies those rows of every K, V and Q tile
+// into LDS (two 1 KB copies of 8 rows each per tile).
 struct Lanes {
   int g, lq, wid, lane;
-  int qr[kQB];                       // query row (inside the tile) of block qb
-  int crow[kCopyInstr];              // tile row copied by this lane, per instruction
-  int ck[kCopyInstr], cv[kCopyInstr];  // logical 16-byte chunk copied (K/Q and V swizzle)
-  uint32_t kofs_g[kCopyInstr], vofs_g[kCopyInstr];  // byte offset of that chunk from the tile's first row
-  int kofs[4][2];                    // K fragment byte offsets inside a stage
-  int vofs[2][4][2];                 // V^T fragment byte offsets inside a stage
+  int qr;                          // query row of this lane inside the tile
+  int crow[2];                     // tile row copied by this lane, per copy instruction
+  int ck[2], cv[2];                // logical 16-byte chunk copied (K/Q and V swizzle)
+  uint32_t kofs_g[2], vofs_g[2];   // byte offset of that chunk from the tile's first row
+  int kofs[4][2];                  // K fragment byte offsets inside a stage
+  int vofs[2][4][2];               // V^T fragment byte offsets inside a stage
 };
 
 __device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
@@ -309,14 +290,13 @@ __device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
   L.wid = tid >> 6;
   L.g = L.lane >> 4;
   L.lq = L.lane & 15;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) L.qr[qb] = L.wid * kRowsPerWave + 16 * qb + L.lq;
-  // Copy role: instruction i moves tile rows kRowsPerWave*wid + 8i .. +7; lane l
-  // lands at byte 16*l of that 1 KB slice (row l/8, physical chunk l%8).
+  L.qr = 16 * L.wid + L.lq;
+  // Copy role: instruction i moves tile rows 16w + 8i .. +7; lane l lands at byte
+  // 16*l of that 1 KB slice (row l/8, physical chunk l%8).
   const int cpos = L.lane & 7;
 #pragma unroll
-  for (int i = 0; i < kCopyInstr; ++i) {
-    L.crow[i] = kRowsPerWave * L.wid + 8 * i + (L.lane >> 3);
+  for (int i = 0; i < 2; ++i) {
+    L.crow[i] = 16 * L.wid + 8 * i + (L.lane >> 3);
     L.ck[i] = cpos ^ swz_k(L.crow[i]);
     L.cv[i] = cpos ^ swz_v(L.crow[i]);
     L.kofs_g[i] = (uint32_t)(L.crow[i] * ldq * 2 + 16 * L.ck[i]);
@@ -344,123 +324,80 @@ __device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
       }
 }
 
-// Issue this wave's copies of key tile j of the current item into stage `dst`.
-// Tiles before the diagonal lie wholly inside the user, so their lanes use the
-// fixed offsets from the tile's first row; the diagonal tile clamps rows past the
-// user's end to its last row (finite data under the causal mask, never another
-// user's rows).
-__device__ __forceinline__ void issue_tile(LDS char* dst, const Lanes& L, const uint16_t* kg, const uint16_t* vg,
-                                           int64_t ldq, int j, int len, bool clamp) {
-  LDS char* sk = dst + kRowsPerWave * L.wid * 128;
-  const uint16_t* kt = kg + (int64_t)j * kTileRows * ldq;
-  const uint16_t* vt = vg + (int64_t)j * kTileRows * ldq;
-#pragma unroll
-  for (int i = 0; i < kCopyInstr; ++i) {
-    uint32_t ko = L.kofs_g[i], vo = L.vofs_g[i];
-    if (clamp) {
-      const int r = min(L.crow[i], len - 1 - j * kTileRows);
-      ko = (uint32_t)(r * ldq * 2 + 16 * L.ck[i]);
-      vo = (uint32_t)(r * ldq * 2 + 16 * L.cv[i]);
-    }
-    copy_to_lds(kt, ko, sk + 1024 * i);
-    copy_to_lds(vt, vo, sk + kTileBytes + 1024 * i);
-  }
-}
-
-// Online-softmax state of one lane for each of its query blocks: the running
-// reference max m (raw score units), the O^T accumulator (dims 16d + 4g + r) and
-// the denominator (every register of l holds it).
+// Online-softmax state of one lane: the running reference max m (raw score
+// units), the O^T accumulator (dims 16d + 4g + r) and the denominator (every
+// register of l holds it).
 struct Acc {
-  float m[kQB];
-  f32x4 o[kQB][4];
-  f32x4 l[kQB];
+  float m;
+  f32x4 o[4];
+  f32x4 l;
 };
 
 // One key tile of one item: S^T = K Q^T, mask (diagonal tile only), softmax
-// update, O^T += V^T P^T and l += 1^T P^T, for every query block of the wave.
+// update, O^T += V^T P^T and l += 1^T P^T.
 template <bool kDiag>
-__device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[kQB][2],
-                                          float sl2, float rescale_thr, Acc& A) {
-  const float NEG_INF = -__builtin_inff();
+__device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2], float sl2,
+                                          float rescale_thr, Acc& A) {
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
-  f32x4 s[kQB][4];
+  f32x4 s[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const bf16x8 k0 = lds_b128(base, L.kofs[b][0]);
     const bf16x8 k1 = lds_b128(base, L.kofs[b][1]);
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      s[qb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], s[qb][b], 0, 0, 0);
-    }
+    s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[b], 0, 0, 0);
   }
   if (kDiag) {  // key kk visible to query qr iff kk <= qr
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (32 * (b >> 1) + 8 * L.g + 4 * (b & 1) + r > L.qr[qb]) s[qb][b][r] = NEG_INF;
+      for (int r = 0; r < 4; ++r)
+        if (32 * (b >> 1) + 8 * L.g + 4 * (b & 1) + r > L.qr) s[b][r] = -__builtin_inff();
   }
-  // Lane-local max over this lane's 16 keys of each query block.  The reference
-  // max m of a query is shared by its 4 lane groups; only when some key exceeds it
-  // by more than the threshold (and on the first tile, m = -inf) is the true row
-  // max formed across the lane groups and m raised, with the accumulators
-  // rescaled.  The common path needs no cross-lane traffic.
-  float lm[kQB];
-  bool raise = false;
+  // Lane-local max over this lane's 16 keys.  The reference max m of a query is
+  // shared by its 4 lane groups; only when some key exceeds it by more than the
+  // threshold (and on the first tile, m = -inf) is the true row max formed across
+  // the lane groups and m raised, with the accumulators rescaled.  The common path
+  // needs no cross-lane traffic.
+  const float x0 = vmax(vmax(s[0][0], s[0][1]), s[0][2]);
+  const float x1 = vmax(vmax(s[0][3], s[1][0]), s[1][1]);
+  const float x2 = vmax(vmax(s[1][2], s[1][3]), s[2][0]);
+  const float x3 = vmax(vmax(s[2][1], s[2][2]), s[2][3]);
+  const float x4 = vmax(vmax(s[3][0], s[3][1]), s[3][2]);
+  const float lm = vmax(vmax(vmax(x0, x1), x2), vmax(vmax(x3, x4), s[3][3]));
+  if (__any(lm > A.m + rescale_thr)) {  // wave-uniform
+    const float mt = max_across_lane_groups(lm);
+    const float mn = fmaxf(A.m, mt);
+    const float alpha = __builtin_amdgcn_exp2f((A.m - mn) * sl2);
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    float x = s[qb][0][0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) x = fmaxf(x, s[qb][e >> 2][e & 3]);
-    lm[qb] = x;
-    raise |= x > A.m[qb] + rescale_thr;
+    for (int d = 0; d < 4; ++d) A.o[d] *= alpha;
+    A.l *= alpha;
+    A.m = mn;
   }
-  if (__any(raise)) {  // wave-uniform
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float mt = max_across_lane_groups(lm[qb]);
-      const float mn = fmaxf(A.m[qb], mt);
-      const float alpha = __builtin_amdgcn_exp2f((A.m[qb] - mn) * sl2);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) A.o[qb][d] *= alpha;
-      A.l[qb] *= alpha;
-      A.m[qb] = mn;
-    }
-  }
+  const float moff = -A.m * sl2;
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     // P^T slots 0..7 of lane group g = keys 32hh + 8g + 0..7 = blocks 2hh, 2hh+1
-    bf16x8 pb[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float moff = -A.m[qb] * sl2;
-      const f32x4& s0 = s[qb][2 * hh];
-      const f32x4& s1 = s[qb][2 * hh + 1];
-      uint4 pw;
-      pw.x = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0], sl2, moff)),
-                         __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
-      pw.y = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2], sl2, moff)),
-                         __builtin_amdgcn_exp2f(__builtin_fmaf(s0[3], sl2, moff)));
-      pw.z = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[0], sl2, moff)),
-                         __builtin_amdgcn_exp2f(__builtin_fmaf(s1[1], sl2, moff)));
-      pw.w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2], sl2, moff)),
-                         __builtin_amdgcn_exp2f(__builtin_fmaf(s1[3], sl2, moff)));
-      pb[qb] = __builtin_bit_cast(bf16x8, pw);
-    }
+    const f32x4& s0 = s[2 * hh];
+    const f32x4& s1 = s[2 * hh + 1];
+    uint4 pw;
+    pw.x = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
+    pw.y = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s0[3], sl2, moff)));
+    pw.z = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[0], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[1], sl2, moff)));
+    pw.w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[3], sl2, moff)));
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const bf16x4 lo = lds_tr16(base, L.vofs[hh][d][0]);
       const bf16x4 hi = lds_tr16(base, L.vofs[hh][d][1]);
       const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-        A.o[qb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb], A.o[qb][d], 0, 0, 0);
+      A.o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, A.o[d], 0, 0, 0);
     }
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) A.l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb], A.l[qb], 0, 0, 0);
+    A.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, A.l, 0, 0, 0);
   }
 }
 
@@ -469,16 +406,22 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
                                                                  const int32_t* __restrict__ count,
                                                                  int n_heads, float sl2,
                                                                  uint16_t* __restrict__ out) {
-  static_assert(kStages >= 2 && kStages <= 4, "ring depth");
-  __shared__ __attribute__((aligned(1024))) Stage ring_lds[kStages];
-  LDS char* const ring = (LDS char*)ring_lds[0].bytes;
-  auto stage = [&](int j) { return ring + (j % kStages) * kStageBytes; };
+  // Two ring stages (K tile then V tile); tile j of an item lives in stage j%2.
+  // The key loop is unrolled by two so that every LDS address is a per-lane
+  // register plus an immediate.
+  __shared__ __attribute__((aligned(1024))) char ring_lds[2 * kStageBytes];
+  LDS char* const st0 = (LDS char*)ring_lds;
+  LDS char* const st1 = st0 + kStageBytes;
 
   const int64_t ldq = 3 * n_heads * kHeadDim;
+  const int64_t ldo = n_heads * kHeadDim;
+  const int hd = n_heads * kHeadDim;
   Lanes L;
   make_lanes(L, ldq);
-  const int64_t ldo = n_heads * kHeadDim;
   const float rescale_thr = kRescaleLog2 / sl2;  // in raw score units
+  // M0 (LDS destination) of this wave's first copy slice in the K half of stage 0;
+  // the second slice is 1 KB further, the V half 8 KB, stage 1 16 KB.
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2048 * L.wid));
 
   // Work assignment.  With the grid a multiple of H, workgroup g always runs head
   // g % H (with H = 8 that is the XCD it sits on) and item slot g / H of each
@@ -508,6 +451,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     const int start = it.z;
     const int len = it.w;
     const int q0 = qt * kTileRows;
+    const int lim = len - 1 - q0;  // the user's last row, relative to the diagonal tile
     // The longest items bound the kernel's critical path: their waves get issue
     // priority over co-resident shorter items.
     if (qt >= 1 && 2 * qt >= qt_max)
@@ -518,73 +462,88 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       __builtin_amdgcn_s_setprio(1);
     else
       __builtin_amdgcn_s_setprio(0);
-    const uint16_t* kg = qkv + (int64_t)start * ldq + n_heads * kHeadDim + h * kHeadDim;
-    const uint16_t* vg = kg + n_heads * kHeadDim;
+    const uint16_t* kg = qkv + (int64_t)start * ldq + hd + h * kHeadDim;
+    const int64_t tstride = (int64_t)kTileRows * ldq;
 
-    // The wave's Q rows go through the K half of the last ring stage: each wave
-    // copies and reads only its own rows, and tile kStages-1 later overwrites
-    // exactly those rows of the same wave, after its Q reads have completed.
-    LDS char* const qstage = ring + (kStages - 1) * kStageBytes;
+    // This wave's copies of key tile jj into the stage at M0 offset `so`.  Tiles
+    // before the diagonal lie wholly inside the user; the diagonal tile clamps rows
+    // past the user's end to its last row (finite data under the causal mask,
+    // never another user's rows).
+    auto issue_tile = [&](uint32_t so, int jj) {
+      const uint16_t* kt = kg + jj * tstride;
+      const uint16_t* vt = kt + hd;
+      if (jj == qt) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = min(L.crow[i], lim);
+          copy_to_lds(kt, (uint32_t)(r * ldq * 2 + 16 * L.ck[i]), m0 + so + 1024 * i);
+          copy_to_lds(vt, (uint32_t)(r * ldq * 2 + 16 * L.cv[i]), m0 + so + kTileBytes + 1024 * i);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          copy_to_lds(kt, L.kofs_g[i], m0 + so + 1024 * i);
+          copy_to_lds(vt, L.vofs_g[i], m0 + so + kTileBytes + 1024 * i);
+        }
+      }
+    };
+
+    // The wave's Q rows go into its own rows of the K half of stage 1, which only
+    // this wave refills (with tile 1), after its Q reads have completed.
     {
-      LDS char* sq = qstage + kRowsPerWave * L.wid * 128;
       const uint16_t* qg = qkv + ((int64_t)start + q0) * ldq + h * kHeadDim;
 #pragma unroll
-      for (int i = 0; i < kCopyInstr; ++i) {
-        const int r = min(L.crow[i], len - 1 - q0);
-        copy_to_lds(qg, (uint32_t)(r * ldq * 2 + 16 * L.ck[i]), sq + 1024 * i);
+      for (int i = 0; i < 2; ++i) {
+        const int r = min(L.crow[i], lim);
+        copy_to_lds(qg, (uint32_t)(r * ldq * 2 + 16 * L.ck[i]), m0 + kStageBytes + 1024 * i);
       }
     }
-    // Prologue: tiles 0 .. kStages-2 (those that exist) into stages 0 .. kStages-2.
-    const int pre = min(qt, kStages - 2);  // index of the last prologue tile
-#pragma unroll
-    for (int j = 0; j <= kStages - 2; ++j)
-      if (j <= pre) issue_tile(ring + j * kStageBytes, L, kg, vg, ldq, j, len, j == qt);
-    wait_tiles_pending(pre + 1);  // this wave's Q rows have landed (all prologue tiles may be in flight)
-    bf16x8 qf[kQB][2];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int row = L.qr[qb];
-      qf[qb][0] = lds_b128(qstage, row * 128 + ((L.g ^ swz_k(row)) << 4));
-      qf[qb][1] = lds_b128(qstage, row * 128 + (((4 + L.g) ^ swz_k(row)) << 4));
-    }
-    wait_vmem_lds<kMaxPending>();  // ... and been read (lgkmcnt) before that stage is refilled
+    issue_tile(0, 0);
+    wait_vmem_lds<4>();  // this wave's Q rows have landed (tile 0's 4 copies may be in flight)
+    bf16x8 qf[2];
+    qf[0] = lds_b128(st1, L.qr * 128 + ((L.g ^ swz_k(L.qr)) << 4));
+    qf[1] = lds_b128(st1, L.qr * 128 + (((4 + L.g) ^ swz_k(L.qr)) << 4));
 
     Acc A;
+    A.m = -__builtin_inff();
+    A.l = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      A.m[qb] = -__builtin_inff();
-      A.l[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int d = 0; d < 4; ++d) A.o[qb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int d = 0; d < 4; ++d) A.o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Tile j lives in stage j % kStages.  Before consuming it, only the copies of
-    // tiles j+1 .. j+kStages-2 (those that exist) may still be in flight: wait
-    // for the rest, then a barrier makes every wave's copies visible and frees
-    // stage (j-1) % kStages for tile j+kStages-1.  Off-diagonal tiles (j < qt)
-    // need no mask; the diagonal tile runs last.
-    for (int j = 0; j < qt; ++j) {
-      wait_tiles_pending_barrier(min(qt - j, kStages - 2));
-      if (j + kStages - 1 <= qt) issue_tile(stage(j + kStages - 1), L, kg, vg, ldq, j + kStages - 1, len,
-                                            j + kStages - 1 == qt);
-      tile_step<false>(stage(j), L, qf, sl2, rescale_thr, A);
+    // Before consuming tile j: wait for this wave's copies of it, then a barrier
+    // makes every wave's copies visible and guarantees that the other stage (tile
+    // j-1, or the Q rows) has been read by every wave, so tile j+1 may refill it.
+    // Off-diagonal tiles (j < qt) need no mask; the diagonal tile runs last.
+    int j = 0;
+    for (; j + 2 <= qt; j += 2) {
+      wait_and_barrier<0>();
+      issue_tile(kStageBytes, j + 1);
+      tile_step<false>(st0, L, qf, sl2, rescale_thr, A);
+      wait_and_barrier<0>();
+      issue_tile(0, j + 2);
+      tile_step<false>(st1, L, qf, sl2, rescale_thr, A);
     }
-    wait_and_barrier<0>();
-    tile_step<true>(stage(qt), L, qf, sl2, rescale_thr, A);
+    if (j < qt) {  // qt odd: tile qt-1 in stage 0, the diagonal tile goes to stage 1
+      wait_and_barrier<0>();
+      issue_tile(kStageBytes, qt);
+      tile_step<false>(st0, L, qf, sl2, rescale_thr, A);
+      wait_and_barrier<0>();
+      tile_step<true>(st1, L, qf, sl2, rescale_thr, A);
+    } else {  // qt even: the diagonal tile is in stage 0
+      wait_and_barrier<0>();
+      tile_step<true>(st0, L, qf, sl2, rescale_thr, A);
+    }
     wait_and_barrier<0>();  // every wave is done with the ring before the next item refills it
 
+    if (L.qr < len - q0) {
+      const float inv = 1.0f / A.l[0];
+      uint16_t* o = out + ((int64_t)start + q0 + L.qr) * ldo + h * kHeadDim + 4 * L.g;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      if (q0 + L.qr[qb] < len) {
-        const float inv = 1.0f / A.l[qb][0];
-        uint16_t* o = out + ((int64_t)start + q0 + L.qr[qb]) * ldo + h * kHeadDim + 4 * L.g;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint2 wv;
-          wv.x = pack_bf16x2(A.o[qb][d][0] * inv, A.o[qb][d][1] * inv);
-          wv.y = pack_bf16x2(A.o[qb][d][2] * inv, A.o[qb][d][3] * inv);
-          *reinterpret_cast<uint2*>(o + 16 * d) = wv;
-        }
+      for (int d = 0; d < 4; ++d) {
+        uint2 wv;
+        wv.x = pack_bf16x2(A.o[d][0] * inv, A.o[d][1] * inv);
+        wv.y = pack_bf16x2(A.o[d][2] * inv, A.o[d][3] * inv);
+        *reinterpret_cast<uint2*>(o + 16 * d) = wv;
       }
     }
   }
@@ -605,6 +564,13 @@ hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* c
                      static_cast<const uint16_t*>(qkv), items, count, n_heads, scale_log2e,
                      static_cast<uint16_t*>(out));
   return hipGetLastError();
+}
+
+int attention_blocks_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel, kAttnThreads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
 }
 
 }  // namespace vlca
