@@ -72,8 +72,13 @@ enum {
 };
 
 /*
- * Forward pass.  Runs the segment scheduler (a compact (user, q-tile) worklist,
- * longest items first) and the attention kernel on `stream`.  The worklist lives
+ * Forward pass.  Runs the segment scheduler (a compact (user, q-tile) worklist:
+ * users grouped by length class floor(log2(q-tiles)), longest class first, each
+ * user's q-tiles adjacent, last q-tile first) and the attention kernel on
+ * `stream`.
+ * Small batches (num_users*ceil(max_seqlen/64) <= 2048, and few enough items per
+ * workgroup) run as one kernel in which every workgroup orders the work itself;
+ * they use no library buffer and never allocate.  Otherwise the worklist lives
  * in a library-owned device buffer kept per (device, stream) and grown on demand:
  * the first call on a stream with a larger num_users*ceil(max_seqlen/64) allocates
  * it (hipMalloc) after synchronising that stream, which is not allowed while the

@@ -106,13 +106,32 @@ def test_constant_v(gpu):
     assert torch.max(torch.abs(out.float() - c.float()[None, :])) <= 2 ** -7 * 3
 
 
-def test_worklist_entry_point_matches_fwd(gpu):
-    w = workloads.make_config(3)
-    say("[case] build_worklist + fwd_with_worklist vs fwd")
+# Batches with users x ceil(max_seqlen/64) <= 2048 run as one kernel that orders
+# its own work; larger ones run the scheduler and the attention kernel over a
+# worklist buffer.  Both must give the same bits as the explicit worklist path.
+WORKLIST_CASES = [
+    ("config 2 (single kernel)", lambda: workloads.make_config(2), None),
+    ("config 3 (scheduler + worklist)", lambda: workloads.make_config(3), None),
+    ("256 users x 8 tiles (single kernel, at the limit)",
+     lambda: workloads.make_from_lengths(list(np.random.default_rng(3).integers(1, 513, 256)), seed=3), 512),
+    ("257 users x 8 tiles (just past the limit)",
+     lambda: workloads.make_from_lengths(list(np.random.default_rng(4).integers(1, 513, 257)), seed=4), 512),
+    ("zero-length users, 3 heads", lambda: workloads.make_from_lengths([0, 70, 0, 0, 5, 200, 0], seed=5, n_heads=3),
+     None),
+    ("one user of 4096 rows (64 q-tiles)", lambda: workloads.make_from_lengths([4096], seed=6), None),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WORKLIST_CASES)))
+def test_worklist_entry_point_matches_fwd(gpu, case):
+    name, make, max_seqlen = WORKLIST_CASES[case]
+    w = make()
+    ms = w.max_seqlen if max_seqlen is None else max_seqlen
+    say(f"[case] build_worklist + fwd_with_worklist vs fwd: {name}")
     qkv, cu = to_gpu(w)
-    a = run_fwd(w, qkv=qkv, cu=cu)
-    items, count = vlca.build_worklist(cu, w.max_seqlen)
-    b = vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, count, scale=w.scale)
+    a = run_fwd(w, max_seqlen=ms, qkv=qkv, cu=cu)
+    items, count = vlca.build_worklist(cu, ms)
+    b = vlca.fwd_with_worklist(qkv, cu, ms, items, count, n_heads=w.n_heads, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b.cpu())
 

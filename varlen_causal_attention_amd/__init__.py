@@ -149,7 +149,7 @@ def fwd(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
 def build_worklist(cu_seqlens, max_seqlen: int) -> Tuple["object", "object"]:
     """Run the segment scheduler alone; returns (items int32 [capacity, 4], count int32 [1]) on the device.
 
-    Rows ``items[:count]`` are (user, q_tile, row_start, length), longest q-tile first;
+    Rows ``items[:count]`` are (user, q_tile, row_start, length) in the scheduler's order;
     later rows are unspecified.
     """
     import torch

@@ -129,6 +129,15 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  // Small batches: one kernel that orders its own work in LDS (no worklist buffer).
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  const int grid = grid_size(dev, num_users, max_seqlen, n_heads);
+  if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
+    if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, out, grid,
+                                     stream) != hipSuccess)
+      return VLCA_ERR_HIP;
+    return VLCA_OK;
+  }
   Workspace* ws = nullptr;
   rc = get_workspace(dev, stream, required_capacity(num_users, max_seqlen), &ws);
   if (rc != VLCA_OK) return rc;

@@ -20,6 +20,12 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int n_heads,
                             float scale_log2e, void* out, int grid, hipStream_t stream);
 
+// Attention alone with the ordering done inside the kernel (no worklist buffer):
+// for batches where fused_fits() holds.
+hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
+                                  int n_heads, float scale_log2e, void* out, int grid, hipStream_t stream);
+bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid);
+
 // Attention workgroups that fit on one CU at once (occupancy of the current device).
 int attention_blocks_per_cu();
 

@@ -51,6 +51,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS __attribute__((address_space(3)))
 typedef LDS bf16x4 lds_bf16x4;
 
@@ -68,8 +69,9 @@ struct Seg {
   int start, len, tiles;
 };
 
-__device__ __forceinline__ Seg segment_of(const int32_t* __restrict__ cu, const int* s_cu, bool cached,
-                                          int u, int total, int max_tiles) {
+template <typename CachePtr>
+__device__ __forceinline__ Seg segment_of(const int32_t* __restrict__ cu, CachePtr s_cu, bool cached, int u, int total,
+                                          int max_tiles) {
   const int a = cached ? s_cu[u] : cu[u];
   const int b = cached ? s_cu[u + 1] : cu[u + 1];
   Seg s{a, 0, 0};
@@ -97,55 +99,54 @@ __device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
 constexpr int kClasses = 13;       // tile counts up to kMaxLevels = 4096 -> classes 0..12
 constexpr int kShortTiles = 16;    // users with more tiles are emitted by a whole wave
 
-// Worklist order: users grouped by length class, highest class first; inside a
-// class users ascend; each user's q-tiles are adjacent, from its last q-tile
-// (the most key tiles) down to q-tile 0.  The first slot of user u is then
+// LDS scratch of the ordering pass for a workgroup of kThreads.
+template <int kThreads>
+struct OrderScratch {
+  int tot[kClasses];                  // tiles per class
+  int base[kClasses];                 // next free slot of each class
+  int wsum[kThreads / 64][kClasses];  // per-wave class sums of the current chunk
+  int long_u[kThreads];               // long users of the current chunk ...
+  int long_off[kThreads];             // ... and their first slots
+  int nlong;
+  int count;                          // items in the list
+};
+
+// Worklist order: users grouped by length class floor(log2(tiles)), highest
+// class first; inside a class users ascend; each user's q-tiles are adjacent,
+// from its last q-tile (the most key tiles) down to q-tile 0.  The first slot of
+// user u is then
 //   sum of the tiles of all higher classes + sum of the tiles of the users
 //   before u in its own class,
 // computed in two passes over the users (class totals, then per-class running
-// sums in chunks of kSchedThreads users).
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ cu, int U,
-                                                                 int max_tiles, int4* __restrict__ items,
-                                                                 int32_t* __restrict__ count) {
-  __shared__ int s_cu[kSchedCache + 1];
-  __shared__ int s_tot[kClasses];                     // tiles per class
-  __shared__ int s_base[kClasses];                    // next free slot of each class
-  __shared__ int s_wsum[kSchedThreads / 64][kClasses];  // per-wave class sums of the current chunk
-  __shared__ int s_long[kSchedThreads];               // long users of the current chunk ...
-  __shared__ int s_longoff[kSchedThreads];            // ... and their first slots
-  __shared__ int s_nlong;
-
+// sums in chunks of kThreads users).  emit(slot, user, q_tile, segment) stores
+// one item; S.count receives the number of items.  All threads of the
+// workgroup must call this (it contains barriers).
+template <int kThreads, typename CachePtr, typename Emit>
+__device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool cached, int nusers, int total,
+                            int max_tiles, LDS OrderScratch<kThreads>* S, Emit emit) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const bool cached = U <= kSchedCache;
-  if (U > 0 && max_tiles > 0 && cached) {
-    for (int i = tid; i <= U; i += kSchedThreads) s_cu[i] = cu[i];
-  }
-  if (tid < kClasses) s_tot[tid] = 0;
+  if (tid < kClasses) S->tot[tid] = 0;
   __syncthreads();
-  const int total = (U > 0 && max_tiles > 0) ? (cached ? s_cu[U] : cu[U]) : 0;
-  const int nusers = max_tiles > 0 ? U : 0;
-
   // Pass 1: tiles per class.
-  for (int u = tid; u < nusers; u += kSchedThreads) {
+  for (int u = tid; u < nusers; u += kThreads) {
     const int t = segment_of(cu, s_cu, cached, u, total, max_tiles).tiles;
-    if (t > 0) atomicAdd(&s_tot[length_class(t)], t);
+    if (t > 0) __atomic_fetch_add(&S->tot[length_class(t)], t, __ATOMIC_RELAXED);
   }
   __syncthreads();
   if (tid == 0) {
     int run = 0;
     for (int c = kClasses - 1; c >= 0; --c) {
-      s_base[c] = run;
-      run += s_tot[c];
+      S->base[c] = run;
+      run += S->tot[c];
     }
-    *count = run;
+    S->count = run;
   }
-
   // Pass 2: slots, chunk by chunk in ascending user order.
-  for (int c0 = 0; c0 < nusers; c0 += kSchedThreads) {
-    if (tid == 0) s_nlong = 0;
-    if (lane < kClasses) s_wsum[wid][lane] = 0;
+  for (int c0 = 0; c0 < nusers; c0 += kThreads) {
+    if (tid == 0) S->nlong = 0;
+    if (lane < kClasses) S->wsum[wid][lane] = 0;
     const int u = c0 + tid;
     Seg s{0, 0, 0};
     if (u < nusers) s = segment_of(cu, s_cu, cached, u, total, max_tiles);
@@ -161,35 +162,59 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
       const int x = mine ? t : 0;
       const int incl = wave_inclusive_sum(x, lane);
       if (mine) pre = incl - x;
-      if (lane == 63) s_wsum[wid][lc] = incl;
+      if (lane == 63) S->wsum[wid][lc] = incl;
       pending &= ~__ballot(mine);
     }
     __syncthreads();
     if (t > 0) {
-      int off = s_base[cl] + pre;
-      for (int w = 0; w < wid; ++w) off += s_wsum[w][cl];
+      int off = S->base[cl] + pre;
+      for (int w = 0; w < wid; ++w) off += S->wsum[w][cl];
       if (t <= kShortTiles) {
-        for (int i = 0; i < t; ++i) items[off + i] = make_int4(u, t - 1 - i, s.start, s.len);
+        for (int i = 0; i < t; ++i) emit(off + i, u, t - 1 - i, s);
       } else {
-        const int k = atomicAdd(&s_nlong, 1);
-        s_long[k] = u;
-        s_longoff[k] = off;
+        const int k = __atomic_fetch_add(&S->nlong, 1, __ATOMIC_RELAXED);
+        S->long_u[k] = u;
+        S->long_off[k] = off;
       }
     }
     __syncthreads();
-    for (int i = wid; i < s_nlong; i += kSchedThreads / 64) {
-      const int lu = s_long[i];
-      const int off = s_longoff[i];
+    const int nlong = S->nlong;
+    for (int i = wid; i < nlong; i += kThreads / 64) {
+      const int lu = S->long_u[i];
+      const int off = S->long_off[i];
       const Seg ls = segment_of(cu, s_cu, cached, lu, total, max_tiles);
-      for (int k = lane; k < ls.tiles; k += 64) items[off + k] = make_int4(lu, ls.tiles - 1 - k, ls.start, ls.len);
+      for (int k = lane; k < ls.tiles; k += 64) emit(off + k, lu, ls.tiles - 1 - k, ls);
     }
     if (tid < kClasses) {
       int sum = 0;
-      for (int w = 0; w < kSchedThreads / 64; ++w) sum += s_wsum[w][tid];
-      s_base[tid] += sum;
+      for (int w = 0; w < kThreads / 64; ++w) sum += S->wsum[w][tid];
+      S->base[tid] += sum;
     }
     __syncthreads();
   }
+  __syncthreads();  // S->count and every emitted item are visible to all threads
+}
+
+// The worklist in global memory: items[slot] = (user, q_tile, row_start, length).
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ cu, int U,
+                                                                 int max_tiles, int4* __restrict__ items,
+                                                                 int32_t* __restrict__ count) {
+  __shared__ int s_cu_lds[kSchedCache + 1];
+  __shared__ OrderScratch<kSchedThreads> S_lds;
+  LDS int* const s_cu = (LDS int*)s_cu_lds;
+  LDS OrderScratch<kSchedThreads>* const S = (LDS OrderScratch<kSchedThreads>*)&S_lds;
+  const bool cached = U <= kSchedCache;
+  if (U > 0 && max_tiles > 0 && cached) {
+    for (int i = threadIdx.x; i <= U; i += kSchedThreads) s_cu[i] = cu[i];
+  }
+  __syncthreads();
+  const int total = (U > 0 && max_tiles > 0) ? (cached ? s_cu[U] : cu[U]) : 0;
+  const int nusers = max_tiles > 0 ? U : 0;
+  order_items<kSchedThreads>(cu, s_cu, cached, nusers, total, max_tiles, S,
+                             [&](int slot, int u, int k, const Seg& sg) {
+                               items[slot] = make_int4(u, k, sg.start, sg.len);
+                             });
+  if (threadIdx.x == 0) *count = S->count;
 }
 
 // ----------------------------------------------------------------- attention
@@ -401,9 +426,21 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
   }
 }
 
+// Rounds a workgroup can run when it builds the worklist itself (kFused).
+constexpr int kFusedRounds = 16;
+// Largest worklist built in LDS by one workgroup (users x max q-tiles).
+constexpr int kFusedItems = 2048;
+
+// kFused = false: walk the first *count items of a worklist built by
+// schedule_kernel.  kFused = true: every workgroup first orders the items of
+// cu_seqlens itself, in LDS that the key ring uses later (only for batches with
+// at most kFusedItems items and kFusedRounds rounds), and keeps the descriptors
+// of its own rounds.
+template <bool kFused>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                                  const int4* __restrict__ items,
                                                                  const int32_t* __restrict__ count,
+                                                                 const int32_t* __restrict__ cu, int U, int max_tiles,
                                                                  int n_heads, float sl2,
                                                                  uint16_t* __restrict__ out) {
   // Two ring stages (K tile then V tile); tile j of an item lives in stage j%2.
@@ -427,16 +464,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   // g % H (with H = 8 that is the XCD it sits on) and item slot g / H of each
   // round; rounds alternate direction (snake), so the workgroups that drew the
   // longest items of round 0 draw the shortest of round 1.
-  const int nitems = *count;
   const int G = gridDim.x;
   const bool by_head = G % n_heads == 0;
   const int slots = by_head ? G / n_heads : G;
   const int slot = by_head ? blockIdx.x / n_heads : blockIdx.x;
   const int head0 = by_head ? blockIdx.x - slot * n_heads : 0;
-  const int qt_max = nitems > 0 ? items[0].y : 0;  // items arrive longest first
-  for (int round = 0;; ++round) {
+  auto work_of = [&](int round, int& item, int& h) {
     const int pos = (round & 1) ? slots - 1 - slot : slot;
-    int item, h;
     if (by_head) {
       item = round * slots + pos;
       h = head0;
@@ -445,11 +479,62 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       item = w / n_heads;
       h = w - item * n_heads;
     }
-    if (item >= nitems) break;
-    const int4 it = items[item];
-    const int qt = it.y;
-    const int start = it.z;
-    const int len = it.w;
+  };
+
+  // kFused: this workgroup's descriptors (q_tile, row_start, length, head), q_tile
+  // < 0 past its last round.
+  __shared__ i32x4 s_desc[kFused ? kFusedRounds : 1];
+  __shared__ int s_qtmax;
+  int nitems = 0, qt_max = 0;
+  if constexpr (kFused) {
+    LDS int* const s_cu = (LDS int*)st0;                       // U + 1 <= kFusedItems + 1 offsets
+    LDS int* const s_list = s_cu + (kFusedItems + 64);         // (user, q_tile) pairs
+    LDS OrderScratch<kAttnThreads>* const S = (LDS OrderScratch<kAttnThreads>*)(s_list + 2 * kFusedItems);
+    const int nusers = max_tiles > 0 ? U : 0;
+    for (int i = threadIdx.x; i <= nusers; i += kAttnThreads) s_cu[i] = cu[i];
+    __syncthreads();
+    const int total = nusers > 0 ? s_cu[nusers] : 0;
+    order_items<kAttnThreads>(cu, s_cu, true, nusers, total, max_tiles, S, [&](int sl, int u, int k, const Seg&) {
+      s_list[2 * sl] = u;
+      s_list[2 * sl + 1] = k;
+    });
+    const int n = S->count;
+    for (int r = threadIdx.x; r < kFusedRounds; r += kAttnThreads) {
+      int item, h;
+      work_of(r, item, h);
+      i32x4 d = {-1, 0, 0, 0};
+      if (item < n) {
+        const int u = s_list[2 * item];
+        d = i32x4{s_list[2 * item + 1], s_cu[u], s_cu[u + 1] - s_cu[u], h};
+      }
+      s_desc[r] = d;
+    }
+    if (threadIdx.x == 0) s_qtmax = n > 0 ? s_list[1] : 0;
+    __syncthreads();  // descriptors visible; the ring is free again
+    qt_max = s_qtmax;
+  } else {
+    nitems = *count;
+    qt_max = nitems > 0 ? items[0].y : 0;  // the first item is a longest user's last q-tile
+  }
+  for (int round = 0;; ++round) {
+    int qt, start, len, h;
+    if constexpr (kFused) {
+      if (round >= kFusedRounds) break;
+      const i32x4 d = s_desc[round];
+      qt = __builtin_amdgcn_readfirstlane(d[0]);
+      if (qt < 0) break;
+      start = __builtin_amdgcn_readfirstlane(d[1]);
+      len = __builtin_amdgcn_readfirstlane(d[2]);
+      h = __builtin_amdgcn_readfirstlane(d[3]);
+    } else {
+      int item;
+      work_of(round, item, h);
+      if (item >= nitems) break;
+      const int4 it = items[item];
+      qt = it.y;
+      start = it.z;
+      len = it.w;
+    }
     const int q0 = qt * kTileRows;
     const int lim = len - 1 - q0;  // the user's last row, relative to the diagonal tile
     // The longest items bound the kernel's critical path: their waves get issue
@@ -560,15 +645,30 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int n_heads,
                             float scale_log2e, void* out, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attention_kernel, dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), items, count, n_heads, scale_log2e,
+  hipLaunchKernelGGL(attention_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream,
+                     static_cast<const uint16_t*>(qkv), items, count, nullptr, 0, 0, n_heads, scale_log2e,
                      static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
+hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
+                                  int n_heads, float scale_log2e, void* out, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(attention_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream,
+                     static_cast<const uint16_t*>(qkv), nullptr, nullptr, cu_seqlens, num_users, max_tiles, n_heads,
+                     scale_log2e, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid) {
+  const int64_t bound = num_users * max_tiles;  // items can not exceed this
+  if (num_users > kFusedItems || bound > kFusedItems) return false;
+  // rounds = ceil(items * H / grid) when the grid is a multiple of H
+  return bound * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
+}
+
 int attention_blocks_per_cu() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel, kAttnThreads, 0) != hipSuccess || n < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<false>, kAttnThreads, 0) != hipSuccess || n < 1)
     n = 1;
   return n;
 }
