@@ -27,7 +27,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 KERNEL_SRC = os.path.join(ROOT, "varlen_causal_attention_amd", "csrc", "vlca_kernels.hip")
-ATTN_KERNEL = "attention_kernel"
+ATTN_KERNEL = "attention_kernel"           # attention_kernel<true>: single-kernel plan; <false>: over a worklist
 
 
 def kernel_source_hash() -> str:
@@ -145,7 +145,7 @@ def summarize_profiles(root: str, config: int) -> None:
              "",
              f"{'kernel':<28} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
     for r in stats:
-        m = re.search(r"([A-Za-z_]\w*)\(", r["Name"])
+        m = re.search(r"([A-Za-z_]\w*(?:<[^>]*>)?)\(", r["Name"])
         short = m.group(1) if m else r["Name"][:28]
         lines.append(f"{short:<28} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.3f} "
                      f"{float(r['MinNs']) / 1e3:>9.3f} {float(r['MaxNs']) / 1e3:>9.3f} "
@@ -159,9 +159,13 @@ def summarize_profiles(root: str, config: int) -> None:
     with open(os.path.join(ROOT, "profiles", f"attention_kernel_{w.name}_trace.txt"), "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
 
-    # HBM traffic: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy's reading.
-    fetch_kib, n_f = _counter_mean(os.path.join(root, "fetch"), ATTN_KERNEL, "FETCH_SIZE")
-    write_kib, n_w = _counter_mean(os.path.join(root, "write"), ATTN_KERNEL, "WRITE_SIZE")
+    # HBM traffic: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy's reading,
+    # for the attention kernel fwd runs (the single-kernel instance when present).
+    fetch_rows = _read_csv(os.path.join(root, "fetch", "run_counter_collection.csv"))
+    kern = f"{ATTN_KERNEL}<true>" if any(f"{ATTN_KERNEL}<true>" in r["Kernel_Name"] for r in fetch_rows) \
+        else f"{ATTN_KERNEL}<false>"
+    fetch_kib, n_f = _counter_mean(os.path.join(root, "fetch"), kern, "FETCH_SIZE")
+    write_kib, n_w = _counter_mean(os.path.join(root, "write"), kern, "WRITE_SIZE")
     copy_f, _ = _counter_mean(os.path.join(root, "copyf"), COPY_KERNEL, "FETCH_SIZE")
     copy_w, _ = _counter_mean(os.path.join(root, "copyw"), COPY_KERNEL, "WRITE_SIZE")
     copy_bytes = 256 * 2**20
@@ -169,7 +173,7 @@ def summarize_profiles(root: str, config: int) -> None:
     w_factor = copy_bytes / (copy_w * 1024.0)
     rd = fetch_kib * 1024.0 * f_factor
     wr = write_kib * 1024.0 * w_factor
-    lines = [f"# rocprofv3 HBM counters for {ATTN_KERNEL}, workload {w.name}",
+    lines = [f"# rocprofv3 HBM counters for {kern}, workload {w.name}",
              f"# command (fetch): {cmds['fetch']}",
              f"# command (write): {cmds['write']}",
              f"# command (copy calibration, fetch): {cmds['copyf']}",
@@ -178,6 +182,7 @@ def summarize_profiles(root: str, config: int) -> None:
              "# 256 MiB device-to-device copy (known bytes), averaged over the dispatches listed.",
              f"kernel_source_sha256_16: {sha}",
              f"workload: {w.name}",
+             f"kernel: {kern}",
              f"fetch_kib_per_dispatch: {fetch_kib:.3f}",
              f"fetch_dispatches: {n_f}",
              f"write_kib_per_dispatch: {write_kib:.3f}",
@@ -269,8 +274,11 @@ def main():
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
 
-    # Dominant kernel alone: the attention kernel over a prebuilt worklist, launched
-    # back to back on the same stream, timed with events on that stream.
+    # Dominant kernel.  When fwd is a single kernel (small batches), the K steps
+    # above are K launches of it back to back: its duration is the step time.
+    # Otherwise the attention kernel alone over a prebuilt worklist, launched back
+    # to back on the same stream, timed with events on that stream.
+    single = vlca.single_kernel(w.num_users, w.max_seqlen, w.n_heads)
     items, _count = vlca.build_worklist(cu, w.max_seqlen)
     for _ in range(args.warmup):
         vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, _count, scale=w.scale, out=out)
@@ -280,9 +288,11 @@ def main():
         vlca.fwd_with_worklist(qkv, cu, w.max_seqlen, items, _count, scale=w.scale, out=out)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_attn = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] step {ms_step * 1e3:.2f} us, attention kernel {ms_attn * 1e3:.2f} us",
-          file=sys.stderr, flush=True)
+    ms_worklist_kernel = e0.elapsed_time(e1) / args.steps
+    ms_attn = ms_step if single else ms_worklist_kernel
+    kernel_name = f"{ATTN_KERNEL}<{'true' if single else 'false'}>"
+    print(f"[bench] step {ms_step * 1e3:.2f} us ({'single kernel' if single else 'scheduler + attention'}), "
+          f"attention kernel over a worklist {ms_worklist_kernel * 1e3:.2f} us", file=sys.stderr, flush=True)
 
     # Cache-cold step: a 512 MiB write evicts L2 and the 256 MiB MALL before each
     # single timed step.
@@ -332,6 +342,7 @@ def main():
             "head_dim": w.head_dim,
             "qkv": f"bf16 [{w.total_tokens}, {3 * w.n_heads * w.head_dim}]",
             "length_law": "lognormal(4.3, 0.9) rescaled, seed 0" if args.config == 2 else "see workloads.py",
+            "launch": "single kernel" if single else "scheduler + attention kernel",
         },
         "cold_ms_per_step": cold_ms,
         "tflops": tflops,
@@ -344,8 +355,9 @@ def main():
             "unit": unit,
             "frac": achieved / peak,
             "traffic": traffic,
-            "kernel": ATTN_KERNEL,
+            "kernel": kernel_name,
             "kernel_us": ms_attn * 1e3,
+            "worklist_kernel_us": ms_worklist_kernel * 1e3,
             "algorithmic_bytes": nbytes,
             "algorithmic_flops": flops,
         },

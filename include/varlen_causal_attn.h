@@ -134,6 +134,16 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
                                     const int32_t* items, int64_t capacity, const int32_t* count,
                                     void* out, hipStream_t stream);
 
+/*
+ * Which launch plan varlen_causal_attn_fwd uses on the current device for these
+ * sizes: writes 1 to *single_kernel when it runs one kernel that orders its own
+ * work (no worklist buffer, never allocates), 0 when it runs the scheduler and
+ * the attention kernel over the library workspace.  No device work; queries the
+ * device's CU count and the kernel's occupancy once.  Errors as for the size
+ * checks of varlen_causal_attn_fwd (VLCA_ERR_HIP without a device).
+ */
+int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads, int* single_kernel);
+
 /* Query rows per work item (and keys per K/V tile): VLCA_TILE_ROWS. */
 int varlen_causal_attn_tile_rows(void);
 

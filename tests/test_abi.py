@@ -111,3 +111,14 @@ def test_build_worklist_and_fwd_worklist_validation():
     assert f(FAKE, FAKE, 4, 40, 8, 64, c, FAKE, 3, FAKE, FAKE * 2, None) == -7
     assert f(FAKE, FAKE, 4, 40, 8, 96, c, FAKE, 5000, FAKE, FAKE * 2, None) == -3
     assert f(None, None, 0, 40, 8, 64, c, None, 0, None, None, None) == 0
+
+
+def test_single_kernel_query_validation():
+    # Size checks run before any HIP call.
+    f = vlca.library().varlen_causal_attn_single_kernel
+    flag = ctypes.c_int(7)
+    assert f(-1, 40, 8, ctypes.byref(flag)) == -2
+    assert f(4, 262145, 8, ctypes.byref(flag)) == -6
+    assert f(4, 40, 0, ctypes.byref(flag)) == -4
+    assert f(4, 40, 8, None) == -1
+    assert flag.value == 7

@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "VlcaError", "library", "library_path", "fwd", "build_worklist", "fwd_with_worklist",
-    "worklist_capacity", "tile_rows", "strerror", "EXPORTED_SYMBOLS",
+    "worklist_capacity", "single_kernel", "tile_rows", "strerror", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +26,7 @@ EXPORTED_SYMBOLS = (
     "varlen_causal_attn_worklist_capacity",
     "varlen_causal_attn_build_worklist",
     "varlen_causal_attn_fwd_worklist",
+    "varlen_causal_attn_single_kernel",
     "varlen_causal_attn_tile_rows",
     "varlen_causal_attn_strerror",
 )
@@ -60,6 +61,8 @@ def library():
     lib.varlen_causal_attn_fwd_worklist.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, i32p,
                                                     ctypes.c_int64, i32p, vp, vp]
     lib.varlen_causal_attn_fwd_worklist.restype = c_int
+    lib.varlen_causal_attn_single_kernel.argtypes = [c_int, c_int, c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.varlen_causal_attn_single_kernel.restype = c_int
     lib.varlen_causal_attn_tile_rows.argtypes = []
     lib.varlen_causal_attn_tile_rows.restype = c_int
     lib.varlen_causal_attn_strerror.argtypes = [c_int]
@@ -74,6 +77,15 @@ def strerror(code: int) -> str:
 
 def tile_rows() -> int:
     return int(library().varlen_causal_attn_tile_rows())
+
+
+def single_kernel(num_users: int, max_seqlen: int, n_heads: int = 8) -> bool:
+    """True when :func:`fwd` runs as one kernel (no worklist buffer) for these sizes on this device."""
+    flag = ctypes.c_int(0)
+    rc = library().varlen_causal_attn_single_kernel(int(num_users), int(max_seqlen), int(n_heads), ctypes.byref(flag))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_single_kernel")
+    return bool(flag.value)
 
 
 def worklist_capacity(num_users: int, max_seqlen: int) -> int:

@@ -181,6 +181,19 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
                      false);
 }
 
+int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads, int* single_kernel) {
+  int rc = check_sizes(num_users, max_seqlen);
+  if (rc != VLCA_OK) return rc;
+  if (single_kernel == nullptr) return VLCA_ERR_NULL_POINTER;
+  if (n_heads < 1 || n_heads > 65536) return VLCA_ERR_N_HEADS;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  const int grid = grid_size(dev, num_users, max_seqlen, n_heads);
+  *single_kernel = (num_users > 0 && max_seqlen > 0 && vlca::fused_fits(num_users, max_tiles, n_heads, grid)) ? 1 : 0;
+  return VLCA_OK;
+}
+
 int varlen_causal_attn_tile_rows(void) { return vlca::kTileRows; }
 
 const char* varlen_causal_attn_strerror(int code) {
