@@ -87,12 +87,16 @@ __device__ __forceinline__ Seg segment_of(const int32_t* __restrict__ cu, CacheP
 // Length class of a user with t >= 1 tiles: floor(log2(t)).
 __device__ __forceinline__ int length_class(int t) { return 31 - __builtin_clz((unsigned)t); }
 
-__device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row
+// broadcasts (no LDS traffic): sums within each row of 16 lanes, then row 0's
+// total is added to row 1 (and row 2's to row 3), then lane 31's to rows 2-3.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return x;
 }
 
@@ -129,19 +133,26 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
   const int wid = tid >> 6;
   if (tid < kClasses) S->tot[tid] = 0;
   __syncthreads();
-  // Pass 1: tiles per class.
-  for (int u = tid; u < nusers; u += kThreads) {
-    const int t = segment_of(cu, s_cu, cached, u, total, max_tiles).tiles;
-    if (t > 0) __atomic_fetch_add(&S->tot[length_class(t)], t, __ATOMIC_RELAXED);
+  // Pass 1: tiles per class (one LDS atomic per class present in a wave).
+  for (int u0 = 0; u0 < nusers; u0 += kThreads) {
+    const int u = u0 + tid;
+    const int t = u < nusers ? segment_of(cu, s_cu, cached, u, total, max_tiles).tiles : 0;
+    const int cl = t > 0 ? length_class(t) : -1;
+    unsigned long long pending = __ballot(t > 0);
+    while (pending) {
+      const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
+      const bool mine = cl == lc;
+      const int sum = __builtin_amdgcn_readlane(wave_inclusive_sum(mine ? t : 0), 63);
+      if (lane == 0) __atomic_fetch_add(&S->tot[lc], sum, __ATOMIC_RELAXED);
+      pending &= ~__ballot(mine);
+    }
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int c = kClasses - 1; c >= 0; --c) {
-      S->base[c] = run;
-      run += S->tot[c];
-    }
-    S->count = run;
+  if (wid == 0) {  // first slot of class c = tiles of all higher classes: lane l holds class 12-l
+    const int v = lane < kClasses ? S->tot[kClasses - 1 - lane] : 0;
+    const int incl = wave_inclusive_sum(v);
+    if (lane < kClasses) S->base[kClasses - 1 - lane] = incl - v;
+    if (lane == kClasses - 1) S->count = incl;
   }
   // Pass 2: slots, chunk by chunk in ascending user order.
   for (int c0 = 0; c0 < nusers; c0 += kThreads) {
@@ -157,10 +168,10 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
     int pre = 0;
     unsigned long long pending = __ballot(t > 0);
     while (pending) {
-      const int lc = __shfl(cl, __builtin_ctzll(pending));
+      const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
       const bool mine = cl == lc;
       const int x = mine ? t : 0;
-      const int incl = wave_inclusive_sum(x, lane);
+      const int incl = wave_inclusive_sum(x);
       if (mine) pre = incl - x;
       if (lane == 63) S->wsum[wid][lc] = incl;
       pending &= ~__ballot(mine);
