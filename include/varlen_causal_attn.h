@@ -76,9 +76,10 @@ enum {
  * users grouped by length class floor(log2(q-tiles)), longest class first, each
  * user's q-tiles adjacent, last q-tile first) and the attention kernel on
  * `stream`.
- * Small batches (num_users*ceil(max_seqlen/64) <= 2048, and few enough items per
- * workgroup) run as one kernel in which every workgroup orders the work itself;
- * they use no library buffer and never allocate.  Otherwise the worklist lives
+ * Small batches (num_users <= 256 and num_users*ceil(max_seqlen/64)*n_heads at most
+ * 16 items per resident workgroup; varlen_causal_attn_single_kernel() tells) run
+ * as one kernel in which every workgroup locates its own items; they use no
+ * library buffer and never allocate.  Otherwise the worklist lives
  * in a library-owned device buffer kept per (device, stream) and grown on demand:
  * the first call on a stream with a larger num_users*ceil(max_seqlen/64) allocates
  * it (hipMalloc) after synchronising that stream, which is not allowed while the

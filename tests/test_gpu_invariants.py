@@ -106,9 +106,10 @@ def test_constant_v(gpu):
     assert torch.max(torch.abs(out.float() - c.float()[None, :])) <= 2 ** -7 * 3
 
 
-# Batches with users x ceil(max_seqlen/64) <= 2048 run as one kernel that orders
-# its own work; larger ones run the scheduler and the attention kernel over a
-# worklist buffer.  Both must give the same bits as the explicit worklist path.
+# Batches with at most 256 users (and few enough items per workgroup) run as one
+# kernel that locates its own work; larger ones run the scheduler and the
+# attention kernel over a worklist buffer.  Both must give the same bits as the
+# explicit worklist path.
 WORKLIST_CASES = [
     ("config 2 (single kernel)", lambda: workloads.make_config(2), None),
     ("config 3 (scheduler + worklist)", lambda: workloads.make_config(3), None),

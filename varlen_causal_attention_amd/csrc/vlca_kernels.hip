@@ -437,16 +437,19 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
   }
 }
 
-// Rounds a workgroup can run when it builds the worklist itself (kFused).
+// Wait for this wave's LDS operations, then a workgroup barrier (no wait on
+// copies in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Rounds a workgroup can run when it orders the work itself (kFused), and the
+// most users that path takes (one per thread).
 constexpr int kFusedRounds = 16;
-// Largest worklist built in LDS by one workgroup (users x max q-tiles).
-constexpr int kFusedItems = 2048;
+constexpr int kFusedUsers = kAttnThreads;
 
 // kFused = false: walk the first *count items of a worklist built by
-// schedule_kernel.  kFused = true: every workgroup first orders the items of
-// cu_seqlens itself, in LDS that the key ring uses later (only for batches with
-// at most kFusedItems items and kFusedRounds rounds), and keeps the descriptors
-// of its own rounds.
+// schedule_kernel.  kFused = true: every workgroup first locates its own items in
+// the same order from cu_seqlens (only for batches with at most kFusedUsers users
+// and kFusedRounds rounds) and keeps their descriptors.
 template <bool kFused>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                                  const int4* __restrict__ items,
@@ -498,30 +501,69 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   __shared__ int s_qtmax;
   int nitems = 0, qt_max = 0;
   if constexpr (kFused) {
-    LDS int* const s_cu = (LDS int*)st0;                       // U + 1 <= kFusedItems + 1 offsets
-    LDS int* const s_list = s_cu + (kFusedItems + 64);         // (user, q_tile) pairs
-    LDS OrderScratch<kAttnThreads>* const S = (LDS OrderScratch<kAttnThreads>*)(s_list + 2 * kFusedItems);
+    // One user per thread.  Each wave finds, per length class present, the
+    // exclusive prefix of its users' q-tile counts (the same order as the
+    // scheduler kernel: classes descending, users ascending, q-tiles of a user
+    // adjacent and descending); per-wave class sums go through LDS; every wave
+    // then forms the class bases itself, so the slot range of each user is known
+    // in registers.  The item of round r is found by a ballot over "my range
+    // holds it".
+    LDS int* const s_wsum = (LDS int*)st0;  // [kWaves][kClasses]
+    const int tid = threadIdx.x;
+    const int lane = L.lane;
+    const int wid = L.wid;
     const int nusers = max_tiles > 0 ? U : 0;
-    for (int i = threadIdx.x; i <= nusers; i += kAttnThreads) s_cu[i] = cu[i];
-    __syncthreads();
-    const int total = nusers > 0 ? s_cu[nusers] : 0;
-    order_items<kAttnThreads>(cu, s_cu, true, nusers, total, max_tiles, S, [&](int sl, int u, int k, const Seg&) {
-      s_list[2 * sl] = u;
-      s_list[2 * sl + 1] = k;
-    });
-    const int n = S->count;
-    for (int r = threadIdx.x; r < kFusedRounds; r += kAttnThreads) {
+    const int total = nusers > 0 ? cu[nusers] : 0;
+    Seg sg{0, 0, 0};
+    if (tid < nusers) sg = segment_of(cu, cu, false, tid, total, max_tiles);
+    const int t = sg.tiles;
+    const int cl = t > 0 ? length_class(t) : -1;
+    if (lane < kClasses) s_wsum[wid * kClasses + lane] = 0;
+    int pre = 0;
+    unsigned long long pending = __ballot(t > 0);
+    while (pending) {
+      const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
+      const bool mine = cl == lc;
+      const int x = mine ? t : 0;
+      const int incl = wave_inclusive_sum(x);
+      if (mine) pre = incl - x;
+      if (lane == 63) s_wsum[wid * kClasses + lc] = incl;
+      pending &= ~__ballot(mine);
+    }
+    lds_barrier();
+    // Class totals and bases (lane l handles class 12-l), the user's first slot.
+    int tot = 0;
+    if (lane < kClasses) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += s_wsum[w * kClasses + kClasses - 1 - lane];
+    }
+    const int incl = wave_inclusive_sum(tot);
+    const int n = __builtin_amdgcn_readlane(incl, kClasses - 1);
+    const int base = incl - tot;  // first slot of class 12-lane
+    // Every lane takes part in the permute (a lane reads the base of its class
+    // from the lane that holds that class).
+    const int cbase = __builtin_amdgcn_ds_bpermute(4 * (kClasses - 1 - (t > 0 ? cl : 0)), base);
+    int off = 0;
+    if (t > 0) {
+      off = cbase + pre;
+      for (int w = 0; w < wid; ++w) off += s_wsum[w * kClasses + cl];
+    }
+    // Items of later rounds lie further down the list, so the first round past
+    // the end closes this workgroup's descriptors.
+    for (int r = 0; r < kFusedRounds; ++r) {
       int item, h;
       work_of(r, item, h);
-      i32x4 d = {-1, 0, 0, 0};
-      if (item < n) {
-        const int u = s_list[2 * item];
-        d = i32x4{s_list[2 * item + 1], s_cu[u], s_cu[u + 1] - s_cu[u], h};
+      if (item >= n) {
+        if (tid == 0) s_desc[r] = i32x4{-1, 0, 0, 0};
+        break;
       }
-      s_desc[r] = d;
+      if (t > 0 && item >= off && item < off + t) s_desc[r] = i32x4{t - 1 - (item - off), sg.start, sg.len, h};
     }
-    if (threadIdx.x == 0) s_qtmax = n > 0 ? s_list[1] : 0;
-    __syncthreads();  // descriptors visible; the ring is free again
+    // The first item (slot 0) is the last q-tile of the first user of the top class.
+    const unsigned long long first = __ballot(t > 0 && off == 0);
+    if (first && lane == __builtin_ctzll(first)) s_qtmax = t - 1;
+    if (tid == 0 && n == 0) s_qtmax = 0;
+    lds_barrier();  // descriptors visible; the ring is free again
     qt_max = s_qtmax;
   } else {
     nitems = *count;
@@ -671,10 +713,9 @@ hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, in
 }
 
 bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid) {
-  const int64_t bound = num_users * max_tiles;  // items can not exceed this
-  if (num_users > kFusedItems || bound > kFusedItems) return false;
-  // rounds = ceil(items * H / grid) when the grid is a multiple of H
-  return bound * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
+  if (num_users > kFusedUsers || grid <= 0) return false;
+  // rounds = ceil(items * H / grid) when the grid is a multiple of H; items <= users x max q-tiles
+  return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
 
 int attention_blocks_per_cu() {
