@@ -390,32 +390,30 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
       for (int r = 0; r < 4; ++r)
         if (32 * (b >> 1) + 8 * L.g + 4 * (b & 1) + r > L.qr) s[b][r] = -__builtin_inff();
   }
-  // Lane-local max over this lane's 16 keys.  The reference max m of a query is
-  // shared by its 4 lane groups; only when some key exceeds it by more than the
-  // threshold (and on the first tile, m = -inf) is the true row max formed across
-  // the lane groups and m raised, with the accumulators rescaled.  The common path
-  // needs no cross-lane traffic.
-  const float x0 = vmax(vmax(s[0][0], s[0][1]), s[0][2]);
-  const float x1 = vmax(vmax(s[0][3], s[1][0]), s[1][1]);
-  const float x2 = vmax(vmax(s[1][2], s[1][3]), s[2][0]);
-  const float x3 = vmax(vmax(s[2][1], s[2][2]), s[2][3]);
-  const float x4 = vmax(vmax(s[3][0], s[3][1]), s[3][2]);
-  const float lm = vmax(vmax(vmax(x0, x1), x2), vmax(vmax(x3, x4), s[3][3]));
-  if (__any(lm > A.m + rescale_thr)) {  // wave-uniform
-    const float mt = max_across_lane_groups(lm);
-    const float mn = fmaxf(A.m, mt);
-    const float alpha = __builtin_amdgcn_exp2f((A.m - mn) * sl2);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) A.o[d] *= alpha;
-    A.l *= alpha;
-    A.m = mn;
-  }
-  const float moff = -A.m * sl2;
+  // The tile is taken in two halves of 32 keys (score blocks 2hh, 2hh+1), so the
+  // second half's QK^T MFMAs run while the first half's softmax is computed.
+  // Lane-local max over this lane's 8 keys of the half.  The reference max m of a
+  // query is shared by its 4 lane groups; only when some key exceeds it by more
+  // than the threshold (and on the first tile, m = -inf; the first half always
+  // holds a visible key of every query) is the true max formed across the lane
+  // groups and m raised, with the accumulators rescaled.  The common path needs
+  // no cross-lane traffic.
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    // P^T slots 0..7 of lane group g = keys 32hh + 8g + 0..7 = blocks 2hh, 2hh+1
     const f32x4& s0 = s[2 * hh];
     const f32x4& s1 = s[2 * hh + 1];
+    const float lm = vmax(vmax(vmax(vmax(s0[0], s0[1]), s0[2]), vmax(vmax(s0[3], s1[0]), s1[1])), vmax(s1[2], s1[3]));
+    if (__any(lm > A.m + rescale_thr)) {  // wave-uniform
+      const float mt = max_across_lane_groups(lm);
+      const float mn = fmaxf(A.m, mt);
+      const float alpha = __builtin_amdgcn_exp2f((A.m - mn) * sl2);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) A.o[d] *= alpha;
+      A.l *= alpha;
+      A.m = mn;
+    }
+    const float moff = -A.m * sl2;
+    // P^T slots 0..7 of lane group g = keys 32hh + 8g + 0..7 = blocks 2hh, 2hh+1
     uint4 pw;
     pw.x = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0], sl2, moff)),
                        __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
