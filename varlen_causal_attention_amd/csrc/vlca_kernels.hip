@@ -230,12 +230,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
 
 // ----------------------------------------------------------------- attention
 
-// XOR swizzles of the 16-byte chunk index inside a 128-byte LDS tile row, chosen
-// so that the fragment reads below touch distinct banks (checked for both 32 and
-// 64 four-byte banks).  K rows are read 16 at a time as rows 8a+4e+{0..3}
-// (a = 0..3); V rows 4 at a time per 16-lane group as rows 8g+{0..3}.
-__device__ __forceinline__ int swz_k(int r) { return ((r & 3) ^ ((r >> 4) & 1)) | (((r >> 3) & 1) << 2); }
-__device__ __forceinline__ int swz_v(int r) { return ((r & 3) ^ ((r >> 3) & 1)) << 1; }
+// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS tile row: chunk
+// c of row r is stored at chunk c ^ (r % 8).  With the fragment row orders below
+// (16 consecutive rows per K read; 4 rows per 16-lane group per V^T read) both
+// the K/Q reads (ds_read_b128) and the V^T reads (ds_read_b64_tr_b16) are free of
+// bank conflicts on gfx950 (4 and 2 LDS cycles per wave instruction).
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 __device__ __forceinline__ bf16x8 lds_b128(const LDS char* base, int byte_off) {
   return __builtin_bit_cast(bf16x8, *(const LDS u32x4*)(base + byte_off));
@@ -312,12 +312,11 @@ __device__ __forceinline__ void copy_to_lds(const void* base, uint32_t voff, uin
 // into LDS (two 1 KB copies of 8 rows each per tile).
 struct Lanes {
   int g, lq, wid, lane;
-  int qr;                          // query row of this lane inside the tile
-  int crow[2];                     // tile row copied by this lane, per copy instruction
-  int ck[2], cv[2];                // logical 16-byte chunk copied (K/Q and V swizzle)
-  uint32_t kofs_g[2], vofs_g[2];   // byte offset of that chunk from the tile's first row
-  int kofs[4][2];                  // K fragment byte offsets inside a stage
-  int vofs[2][4][2];               // V^T fragment byte offsets inside a stage
+  int qr;                 // query row of this lane inside the tile
+  int crow[2];            // tile row copied by this lane, per copy instruction
+  uint32_t cofs_g[2];     // byte offset of the copied 16-byte chunk from the tile's first row
+  int kofs[2];            // K fragment byte offsets inside a stage (block 0; block b: + 2048 b)
+  int vofs[4];            // V^T fragment byte offsets inside a stage (dim block d; + 4096 hh + 2048 s)
 };
 
 __device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
@@ -328,36 +327,31 @@ __device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
   L.lq = L.lane & 15;
   L.qr = 16 * L.wid + L.lq;
   // Copy role: instruction i moves tile rows 16w + 8i .. +7; lane l lands at byte
-  // 16*l of that 1 KB slice (row l/8, physical chunk l%8).
-  const int cpos = L.lane & 7;
+  // 16*l of that 1 KB slice (row l/8, physical chunk l%8, logical chunk
+  // (l%8) ^ (row%8)).
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     L.crow[i] = 16 * L.wid + 8 * i + (L.lane >> 3);
-    L.ck[i] = cpos ^ swz_k(L.crow[i]);
-    L.cv[i] = cpos ^ swz_v(L.crow[i]);
-    L.kofs_g[i] = (uint32_t)(L.crow[i] * ldq * 2 + 16 * L.ck[i]);
-    L.vofs_g[i] = (uint32_t)(L.crow[i] * ldq * 2 + 16 * L.cv[i]);
+    L.cofs_g[i] = (uint32_t)(L.crow[i] * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i])));
   }
-  // K fragment rows: S^T block b (keys 32h..32h+31 with h = b/2, e = b%2), MFMA row
-  // lq <- key 32h + 8(lq/4) + 4e + lq%4; its output reg r in lane group g is then
-  // key 32h + 8g + 4e + r, the order ds_read_b64_tr_b16 gives V^T below.
+  // K fragments: S^T block b covers keys 16b .. 16b+15 in order (MFMA row lq <-
+  // key 16b + lq), so output reg r in lane group g is key 16b + 4g + r.  The lane
+  // reads dims 8g .. 8g+7 (k-step 0) and 32+8g .. (k-step 1) of that row.
+  L.kofs[0] = L.lq * 128 + ((L.g ^ swz(L.lq)) << 4);
+  L.kofs[1] = L.lq * 128 + (((4 + L.g) ^ swz(L.lq)) << 4);
+  // V^T fragments for keys 32hh .. 32hh+31 in the P^T slot order of lane group g:
+  // slots 0..3 = keys 32hh + 4g + 0..3 (score block 2hh), slots 4..7 = keys
+  // 32hh + 16 + 4g + 0..3 (block 2hh+1).  ds_read_b64_tr_b16 gives lane i of a
+  // 16-lane group element i%4 of source lanes {i/4, 4+i/4, 8+i/4, 12+i/4}; with
+  // source lane j reading key row 4g + j/4, dims 16d + 4(j%4) .. +3, lane i gets
+  // the 4 keys of dim 16d + i.  The second half (slots 4..7) is 16 rows on
+  // (+2048 bytes), the second 32 keys 32 rows on (+4096): neither changes row%8.
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int rho = 32 * (b >> 1) + 8 * (L.lq >> 2) + 4 * (b & 1) + (L.lq & 3);
-    L.kofs[b][0] = rho * 128 + ((L.g ^ swz_k(rho)) << 4);
-    L.kofs[b][1] = rho * 128 + (((4 + L.g) ^ swz_k(rho)) << 4);
+  for (int d = 0; d < 4; ++d) {
+    const int rho = 4 * L.g + (L.lq >> 2);
+    const int chunk = 2 * d + ((L.lq & 3) >> 1);
+    L.vofs[d] = kTileBytes + rho * 128 + ((chunk ^ swz(rho)) << 4) + 8 * (L.lq & 1);
   }
-  // V^T fragment sources: keys 32h + 8g + lq/4 (+4), dims 16d + 4(lq%4) .. +3.
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int rho = 32 * h + 8 * L.g + (L.lq >> 2) + 4 * s;
-        const int chunk = 2 * d + ((L.lq & 3) >> 1);
-        L.vofs[h][d][s] = kTileBytes + rho * 128 + ((chunk ^ swz_v(rho)) << 4) + 8 * (L.lq & 1);
-      }
 }
 
 // Online-softmax state of one lane: the running reference max m (raw score
@@ -378,8 +372,8 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
   f32x4 s[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const bf16x8 k0 = lds_b128(base, L.kofs[b][0]);
-    const bf16x8 k1 = lds_b128(base, L.kofs[b][1]);
+    const bf16x8 k0 = lds_b128(base, L.kofs[0] + 2048 * b);
+    const bf16x8 k1 = lds_b128(base, L.kofs[1] + 2048 * b);
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[b], 0, 0, 0);
   }
@@ -388,7 +382,7 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (32 * (b >> 1) + 8 * L.g + 4 * (b & 1) + r > L.qr) s[b][r] = -__builtin_inff();
+        if (16 * b + 4 * L.g + r > L.qr) s[b][r] = -__builtin_inff();
   }
   // The tile is taken in two halves of 32 keys (score blocks 2hh, 2hh+1), so the
   // second half's QK^T MFMAs run while the first half's softmax is computed.
@@ -413,7 +407,8 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
       A.m = mn;
     }
     const float moff = -A.m * sl2;
-    // P^T slots 0..7 of lane group g = keys 32hh + 8g + 0..7 = blocks 2hh, 2hh+1
+    // P^T slots 0..3 of lane group g = keys 32hh + 4g + 0..3 (block 2hh), slots
+    // 4..7 = keys 32hh + 16 + 4g + 0..3 (block 2hh+1)
     uint4 pw;
     pw.x = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0], sl2, moff)),
                        __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
@@ -426,8 +421,8 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const bf16x4 lo = lds_tr16(base, L.vofs[hh][d][0]);
-      const bf16x4 hi = lds_tr16(base, L.vofs[hh][d][1]);
+      const bf16x4 lo = lds_tr16(base, L.vofs[d] + 4096 * hh);
+      const bf16x4 hi = lds_tr16(base, L.vofs[d] + 4096 * hh + 2048);
       const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       A.o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, A.o[d], 0, 0, 0);
     }
@@ -612,14 +607,15 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = min(L.crow[i], lim);
-          copy_to_lds(kt, (uint32_t)(r * ldq * 2 + 16 * L.ck[i]), m0 + so + 1024 * i);
-          copy_to_lds(vt, (uint32_t)(r * ldq * 2 + 16 * L.cv[i]), m0 + so + kTileBytes + 1024 * i);
+          const uint32_t o = (uint32_t)(r * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i])));
+          copy_to_lds(kt, o, m0 + so + 1024 * i);
+          copy_to_lds(vt, o, m0 + so + kTileBytes + 1024 * i);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          copy_to_lds(kt, L.kofs_g[i], m0 + so + 1024 * i);
-          copy_to_lds(vt, L.vofs_g[i], m0 + so + kTileBytes + 1024 * i);
+          copy_to_lds(kt, L.cofs_g[i], m0 + so + 1024 * i);
+          copy_to_lds(vt, L.cofs_g[i], m0 + so + kTileBytes + 1024 * i);
         }
       }
     };
@@ -631,14 +627,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = min(L.crow[i], lim);
-        copy_to_lds(qg, (uint32_t)(r * ldq * 2 + 16 * L.ck[i]), m0 + kStageBytes + 1024 * i);
+        copy_to_lds(qg, (uint32_t)(r * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i]))), m0 + kStageBytes + 1024 * i);
       }
     }
     issue_tile(0, 0);
     wait_vmem_lds<4>();  // this wave's Q rows have landed (tile 0's 4 copies may be in flight)
     bf16x8 qf[2];
-    qf[0] = lds_b128(st1, L.qr * 128 + ((L.g ^ swz_k(L.qr)) << 4));
-    qf[1] = lds_b128(st1, L.qr * 128 + (((4 + L.g) ^ swz_k(L.qr)) << 4));
+    qf[0] = lds_b128(st1, L.qr * 128 + ((L.g ^ swz(L.qr)) << 4));
+    qf[1] = lds_b128(st1, L.qr * 128 + (((4 + L.g) ^ swz(L.qr)) << 4));
 
     Acc A;
     A.m = -__builtin_inff();
