@@ -24,7 +24,7 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
-std::map<int, int> g_resident;  // device -> resident attention workgroups
+std::map<int, int> g_resident;  // 2*device + fused -> resident attention workgroups
 
 int64_t max_tiles_of(int max_seqlen) { return (static_cast<int64_t>(max_seqlen) + vlca::kTileRows - 1) / vlca::kTileRows; }
 
@@ -52,20 +52,22 @@ int check_attention_args(const void* qkv, const int32_t* cu_seqlens, int num_use
   return VLCA_OK;
 }
 
-// Resident attention workgroups per device: CUs x workgroups per CU.
-int resident_blocks(int dev) {
+// Resident attention workgroups per device: CUs x workgroups per CU, for the
+// kernel over a worklist or the single-kernel variant.
+int resident_blocks(int dev, bool fused) {
   std::lock_guard<std::mutex> lk(g_mu);
-  auto it = g_resident.find(dev);
+  const int key = 2 * dev + (fused ? 1 : 0);
+  auto it = g_resident.find(key);
   if (it != g_resident.end()) return it->second;
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  const int r = n * vlca::attention_blocks_per_cu();
-  g_resident[dev] = r;
+  const int r = n * vlca::attention_blocks_per_cu(fused);
+  g_resident[key] = r;
   return r;
 }
 
-int grid_size(int dev, int num_users, int max_seqlen, int n_heads) {
-  int64_t g = resident_blocks(dev);
+int grid_size(int dev, int num_users, int max_seqlen, int n_heads, bool fused) {
+  int64_t g = resident_blocks(dev, fused);
   if (g > vlca::kMaxGrid) g = vlca::kMaxGrid;
   g -= g % 8;  // keeps w % 8 == blockIdx.x % 8 (one head per XCD when H = 8)
   if (g < 8) g = 8;
@@ -112,7 +114,7 @@ int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int m
     if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items, count, stream) != hipSuccess)
       return VLCA_ERR_HIP;
   }
-  const int grid = grid_size(dev, num_users, max_seqlen, n_heads);
+  const int grid = grid_size(dev, num_users, max_seqlen, n_heads, false);
   if (vlca::launch_attention(qkv, items, count, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
@@ -129,9 +131,9 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
-  // Small batches: one kernel that orders its own work in LDS (no worklist buffer).
+  // Small batches: one kernel that locates its own work (no worklist buffer).
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
-  const int grid = grid_size(dev, num_users, max_seqlen, n_heads);
+  const int grid = grid_size(dev, num_users, max_seqlen, n_heads, true);
   if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
     if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, out, grid,
                                      stream) != hipSuccess)
@@ -189,7 +191,7 @@ int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads,
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
-  const int grid = grid_size(dev, num_users, max_seqlen, n_heads);
+  const int grid = grid_size(dev, num_users, max_seqlen, n_heads, true);
   *single_kernel = (num_users > 0 && max_seqlen > 0 && vlca::fused_fits(num_users, max_tiles, n_heads, grid)) ? 1 : 0;
   return VLCA_OK;
 }

@@ -26,7 +26,8 @@ hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, in
                                   int n_heads, float scale_log2e, void* out, int grid, hipStream_t stream);
 bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid);
 
-// Attention workgroups that fit on one CU at once (occupancy of the current device).
-int attention_blocks_per_cu();
+// Attention workgroups that fit on one CU at once (occupancy of the current device),
+// for the kernel over a worklist or the single-kernel variant.
+int attention_blocks_per_cu(bool fused);
 
 }  // namespace vlca

@@ -712,10 +712,11 @@ bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t g
   return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
 
-int attention_blocks_per_cu() {
+int attention_blocks_per_cu(bool fused) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<false>, kAttnThreads, 0) != hipSuccess || n < 1)
-    n = 1;
+  const hipError_t e = fused ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<true>, kAttnThreads, 0)
+                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<false>, kAttnThreads, 0);
+  if (e != hipSuccess || n < 1) n = 1;
   return n;
 }
 
