@@ -457,6 +457,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   LDS char* const st0 = (LDS char*)ring_lds;
   LDS char* const st1 = st0 + kStageBytes;
 
+  // Until its first item is known, a workgroup runs at the highest wave priority:
+  // co-resident workgroups already inside long items (raised below) must not
+  // starve the short work that precedes every item.
+  __builtin_amdgcn_s_setprio(3);
   const int64_t ldq = 3 * n_heads * kHeadDim;
   const int64_t ldo = n_heads * kHeadDim;
   const int hd = n_heads * kHeadDim;
