@@ -84,6 +84,28 @@ def test_length_one_rows_exact(gpu):
             assert torch.equal(out[r], w.qkv_bf16[r, 1024:])
 
 
+def test_many_rounds_per_workgroup(gpu):
+    # 70000 one-row users plus a few longer ones: about 550 items per workgroup
+    # slot, past the descriptors a workgroup caches in LDS, and more users than
+    # the scheduler caches in LDS.  One-row users return their own V row exactly;
+    # the longer users are checked against the oracle.
+    lengths = [1] * 70000
+    for pos, L in ((0, 130), (35000, 257), (69999, 64)):
+        lengths[pos] = L
+    w = workloads.make_from_lengths(lengths, seed=9)
+    say(f"[case] many rounds: {len(lengths)} users, {w.total_tokens} rows")
+    out = run_fwd(w)
+    cu = w.cu_seqlens
+    ones = np.nonzero(np.diff(cu) == 1)[0]
+    rows = torch.from_numpy(cu[ones].astype(np.int64))
+    assert torch.equal(out[rows], w.qkv_bf16[rows, 1024:])
+    q = w.qkv_bf16.to(torch.float64).numpy()
+    for pos in (0, 35000, 69999):
+        r = slice(int(cu[pos]), int(cu[pos + 1]))
+        ref = oracle.varlen_causal_attention_rows(q, cu, np.arange(r.start, r.stop), w.n_heads, w.head_dim, w.scale)
+        assert_close(out[r], ref, f"user {pos}")
+
+
 def test_zero_query_gives_running_mean(gpu):
     w = workloads.make_from_lengths([5, 90, 200, 1], seed=3)
     w.qkv_bf16[:, :512] = 0

@@ -536,6 +536,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     }
     const int incl = wave_inclusive_sum(tot);
     const int n = __builtin_amdgcn_readlane(incl, kClasses - 1);
+    {  // a workgroup past the last item (the grid may exceed the work) leaves now
+      int item0, h0;
+      work_of(0, item0, h0);
+      if (item0 >= n) return;  // uniform across the workgroup
+    }
     const int base = incl - tot;  // first slot of class 12-lane
     // Every lane takes part in the permute (a lane reads the base of its class
     // from the lane that holds that class).
