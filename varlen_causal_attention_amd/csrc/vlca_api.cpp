@@ -16,9 +16,12 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Bytes after the workspace's items: the count, then from the next 256-byte
+// boundary the work counters (kQueueStride int32 apart).
+constexpr size_t kWorkspaceTail = (1 + vlca::kQueues) * vlca::kQueueStride * sizeof(int32_t);
 
 struct Workspace {
-  int4* items = nullptr;     // capacity items, then one int32 count
+  int4* items = nullptr;     // capacity items, the int32 count, then the work counters
   int64_t capacity = 0;
 };
 
@@ -95,7 +98,8 @@ int get_workspace(int dev, hipStream_t stream, int64_t capacity, Workspace** out
       ws.capacity = 0;
     }
     void* p = nullptr;
-    if (hipMalloc(&p, static_cast<size_t>(cap) * sizeof(int4) + 256) != hipSuccess) return VLCA_ERR_WORKSPACE;
+    if (hipMalloc(&p, static_cast<size_t>(cap) * sizeof(int4) + kWorkspaceTail) != hipSuccess)
+      return VLCA_ERR_WORKSPACE;
     ws.items = static_cast<int4*>(p);
     ws.capacity = cap;
   }
@@ -105,17 +109,20 @@ int get_workspace(int dev, hipStream_t stream, int64_t capacity, Workspace** out
 
 int32_t* workspace_count(const Workspace* ws) { return reinterpret_cast<int32_t*>(ws->items + ws->capacity); }
 
+// Scheduler (when schedule) then attention.  queue: the library workspace's work
+// counters (dynamic assignment, zeroed by the scheduler), or null for a caller's
+// worklist (fixed assignment).
 int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, float scale,
-                int4* items, int32_t* count, void* out, hipStream_t stream, bool schedule) {
+                int4* items, int32_t* count, int32_t* queue, void* out, hipStream_t stream, bool schedule) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   if (schedule) {
-    if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items, count, stream) != hipSuccess)
+    if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items, count, queue, stream) != hipSuccess)
       return VLCA_ERR_HIP;
   }
   const int grid = grid_size(dev, num_users, max_seqlen, n_heads, false);
-  if (vlca::launch_attention(qkv, items, count, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
+  if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
@@ -143,8 +150,8 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   Workspace* ws = nullptr;
   rc = get_workspace(dev, stream, required_capacity(num_users, max_seqlen), &ws);
   if (rc != VLCA_OK) return rc;
-  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, ws->items, workspace_count(ws), out,
-                     stream, true);
+  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, ws->items, workspace_count(ws),
+                     workspace_count(ws) + vlca::kQueueStride, out, stream, true);
 }
 
 int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity) {
@@ -164,8 +171,8 @@ int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, 
     return VLCA_ERR_NULL_POINTER;
   if (capacity < need) return VLCA_ERR_CAPACITY;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
-  if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, reinterpret_cast<int4*>(items), count, stream) !=
-      hipSuccess)
+  if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, reinterpret_cast<int4*>(items), count, nullptr,
+                            stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
@@ -179,8 +186,8 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
   if (num_users > 0 && capacity < required_capacity(num_users, max_seqlen)) return VLCA_ERR_CAPACITY;
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale,
-                     reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), out, stream,
-                     false);
+                     reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), nullptr, out,
+                     stream, false);
 }
 
 int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads, int* single_kernel) {

@@ -12,12 +12,21 @@ constexpr int kHeadDim = 64;
 constexpr int kMaxLevels = 4096;     // q-tiles per user the scheduler can order
 constexpr int kMaxGrid = 4096;       // persistent grid cap
 
-// Scheduler: one workgroup builds the (user, q_tile, row_start, length) list.
-hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles,
-                           int4* items, int32_t* count, hipStream_t stream);
+// Work counters of the attention kernel's dynamic assignment (one per head, or
+// one over all (item, head) pairs when there are more heads), each alone in its
+// own 256-byte block: counter q is queue[q * kQueueStride].
+constexpr int kQueues = 8;
+constexpr int kQueueStride = 64;
 
-// Attention: persistent grid walking the first *count items (heads fastest).
-hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int n_heads,
+// Scheduler: one workgroup builds the (user, q_tile, row_start, length) list and,
+// when queue is not null, zeroes the kQueues counters at queue.
+hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles,
+                           int4* items, int32_t* count, int32_t* queue, hipStream_t stream);
+
+// Attention: persistent grid walking the first *count items.  queue null: a fixed
+// assignment of items to workgroups; otherwise workgroups claim items from the
+// zeroed counters at queue (reset by launch_schedule).
+hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue, int n_heads,
                             float scale_log2e, void* out, int grid, hipStream_t stream);
 
 // Attention alone with the ordering done inside the kernel (no worklist buffer):

@@ -209,7 +209,10 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
 // The worklist in global memory: items[slot] = (user, q_tile, row_start, length).
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ cu, int U,
                                                                  int max_tiles, int4* __restrict__ items,
-                                                                 int32_t* __restrict__ count) {
+                                                                 int32_t* __restrict__ count,
+                                                                 int32_t* __restrict__ queue) {
+  // The attention kernel's work counters start at zero.
+  if (queue != nullptr && threadIdx.x < kQueues) queue[threadIdx.x * kQueueStride] = 0;
   __shared__ int s_cu_lds[kSchedCache + 1];
   __shared__ OrderScratch<kSchedThreads> S_lds;
   LDS int* const s_cu = (LDS int*)s_cu_lds;
@@ -359,6 +362,8 @@ __device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
 // register of l holds it).
 struct Acc {
   float m;
+  float moff;  // -m * sl2: the exponent offset of the weights
+  float mthr;  // m + rescale threshold: keys above it raise m
   f32x4 o[4];
   f32x4 l;
 };
@@ -366,9 +371,8 @@ struct Acc {
 // One key tile of one item: S^T = K Q^T, mask (diagonal tile only), softmax
 // update, O^T += V^T P^T and l += 1^T P^T.
 template <bool kDiag>
-__device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2], float sl2,
-                                          float rescale_thr, Acc& A) {
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+__device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2],
+                                          const bf16x8& ones, float sl2, float rescale_thr, Acc& A) {
   f32x4 s[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -397,7 +401,7 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
     const f32x4& s0 = s[2 * hh];
     const f32x4& s1 = s[2 * hh + 1];
     const float lm = vmax(vmax(vmax(vmax(s0[0], s0[1]), s0[2]), vmax(vmax(s0[3], s1[0]), s1[1])), vmax(s1[2], s1[3]));
-    if (__any(lm > A.m + rescale_thr)) {  // wave-uniform
+    if (__any(lm > A.mthr)) {  // wave-uniform
       const float mt = max_across_lane_groups(lm);
       const float mn = fmaxf(A.m, mt);
       const float alpha = __builtin_amdgcn_exp2f((A.m - mn) * sl2);
@@ -405,8 +409,10 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
       for (int d = 0; d < 4; ++d) A.o[d] *= alpha;
       A.l *= alpha;
       A.m = mn;
+      A.moff = -mn * sl2;
+      A.mthr = mn + rescale_thr;
     }
-    const float moff = -A.m * sl2;
+    const float moff = A.moff;
     // P^T slots 0..3 of lane group g = keys 32hh + 4g + 0..3 (block 2hh), slots
     // 4..7 = keys 32hh + 16 + 4g + 0..3 (block 2hh+1)
     uint4 pw;
@@ -447,6 +453,7 @@ template <bool kFused>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                                  const int4* __restrict__ items,
                                                                  const int32_t* __restrict__ count,
+                                                                 int32_t* __restrict__ queue,
                                                                  const int32_t* __restrict__ cu, int U, int max_tiles,
                                                                  int n_heads, float sl2,
                                                                  uint16_t* __restrict__ out) {
@@ -467,6 +474,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   Lanes L;
   make_lanes(L, ldq);
   const float rescale_thr = kRescaleLog2 / sl2;  // in raw score units
+  // The all-ones A operand of the denominator MFMA, kept in registers (the empty
+  // asm hides the constant, so it is not rebuilt before every use).
+  bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  asm volatile("" : "+v"(ones));
   // M0 (LDS destination) of this wave's first copy slice in the K half of stage 0;
   // the second slice is 1 KB further, the V half 8 KB, stage 1 16 KB.
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2048 * L.wid));
@@ -571,6 +582,24 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     nitems = *count;
     qt_max = nitems > 0 ? items[0].y : 0;  // the first item is a longest user's last q-tile
   }
+  // Dynamic assignment (worklist path with work counters): instead of the fixed
+  // snake, a workgroup takes the next unclaimed item from a counter in global
+  // memory, so workgroups that drew short items take more of them.  With one
+  // head per workgroup (by_head, H <= kQueues) each head has its own counter and
+  // items are taken in list order (users kept together, so later q-tiles find
+  // the user's K/V in the L2 of the XCD serving that head); otherwise one counter
+  // runs over all (item, head) pairs, heads fastest.  Thread 0 claims the next
+  // item while the current one runs; LDS passes it to all waves at the item's
+  // last barrier.
+  const bool dyn = !kFused && queue != nullptr;
+  const bool per_head = by_head && n_heads <= kQueues;
+  int32_t* const qctr = dyn ? queue + (per_head ? head0 : 0) * kQueueStride : nullptr;
+  __shared__ int s_next;
+  int claimed = 0;
+  if (dyn) {
+    if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+  }
   for (int round = 0;; ++round) {
     int qt, start, len, h;
     if constexpr (kFused) {
@@ -583,8 +612,21 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       h = __builtin_amdgcn_readfirstlane(d[3]);
     } else {
       int item;
-      work_of(round, item, h);
-      if (item >= nitems) break;
+      if (dyn) {
+        const int w = __builtin_amdgcn_readfirstlane(s_next);
+        if (per_head) {
+          item = w;
+          h = head0;
+        } else {
+          item = w / n_heads;
+          h = w - item * n_heads;
+        }
+        if (item >= nitems) break;
+        if (threadIdx.x == 0) claimed = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        work_of(round, item, h);
+        if (item >= nitems) break;
+      }
       const int4 it = items[item];
       qt = it.y;
       start = it.z;
@@ -647,6 +689,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
 
     Acc A;
     A.m = -__builtin_inff();
+    A.moff = __builtin_inff();
+    A.mthr = -__builtin_inff();
     A.l = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < 4; ++d) A.o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -659,21 +703,24 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     for (; j + 2 <= qt; j += 2) {
       wait_and_barrier<0>();
       issue_tile(kStageBytes, j + 1);
-      tile_step<false>(st0, L, qf, sl2, rescale_thr, A);
+      tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
       wait_and_barrier<0>();
       issue_tile(0, j + 2);
-      tile_step<false>(st1, L, qf, sl2, rescale_thr, A);
+      tile_step<false>(st1, L, qf, ones, sl2, rescale_thr, A);
     }
     if (j < qt) {  // qt odd: tile qt-1 in stage 0, the diagonal tile goes to stage 1
       wait_and_barrier<0>();
       issue_tile(kStageBytes, qt);
-      tile_step<false>(st0, L, qf, sl2, rescale_thr, A);
+      tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
       wait_and_barrier<0>();
-      tile_step<true>(st1, L, qf, sl2, rescale_thr, A);
+      tile_step<true>(st1, L, qf, ones, sl2, rescale_thr, A);
     } else {  // qt even: the diagonal tile is in stage 0
       wait_and_barrier<0>();
-      tile_step<true>(st0, L, qf, sl2, rescale_thr, A);
+      tile_step<true>(st0, L, qf, ones, sl2, rescale_thr, A);
     }
+    // The claim made at the item's start is passed on; every wave read s_next
+    // before this item's first barrier.
+    if (dyn && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring before the next item refills it
 
     if (L.qr < len - q0) {
@@ -693,16 +740,16 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles, int4* items, int32_t* count,
-                           hipStream_t stream) {
+                           int32_t* queue, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens, num_users, max_tiles,
-                     items, count);
+                     items, count, queue);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int n_heads,
+hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue, int n_heads,
                             float scale_log2e, void* out, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(attention_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), items, count, nullptr, 0, 0, n_heads, scale_log2e,
+                     static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, scale_log2e,
                      static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
@@ -710,8 +757,8 @@ hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* c
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
                                   int n_heads, float scale_log2e, void* out, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(attention_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), nullptr, nullptr, cu_seqlens, num_users, max_tiles, n_heads,
-                     scale_log2e, static_cast<uint16_t*>(out));
+                     static_cast<const uint16_t*>(qkv), nullptr, nullptr, nullptr, cu_seqlens, num_users, max_tiles,
+                     n_heads, scale_log2e, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
