@@ -142,6 +142,15 @@ WORKLIST_CASES = [
     ("zero-length users, 3 heads", lambda: workloads.make_from_lengths([0, 70, 0, 0, 5, 200, 0], seed=5, n_heads=3),
      None),
     ("one user of 4096 rows (64 q-tiles)", lambda: workloads.make_from_lengths([4096], seed=6), None),
+    # Scheduler plan (more than 256 users) with counters that cannot be one per head:
+    # 3 heads (the grid is not a multiple of the head count) and 16 heads (more heads
+    # than counters) both claim (item, head) pairs from a single counter.
+    ("300 users, 3 heads (scheduler plan, one counter)",
+     lambda: workloads.make_from_lengths(list(np.random.default_rng(7).integers(0, 101, 300)), seed=7, n_heads=3),
+     None),
+    ("300 users, 16 heads (scheduler plan, one counter)",
+     lambda: workloads.make_from_lengths(list(np.random.default_rng(8).integers(0, 101, 300)), seed=8, n_heads=16),
+     None),
 ]
 
 

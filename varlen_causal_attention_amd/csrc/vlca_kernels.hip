@@ -634,9 +634,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     }
     const int q0 = qt * kTileRows;
     const int lim = len - 1 - q0;  // the user's last row, relative to the diagonal tile
-    // The longest items bound the kernel's critical path: their waves get issue
-    // priority over co-resident shorter items.
-    if (qt >= 1 && 2 * qt >= qt_max)
+    // Scheduler plan: the longest items bound the kernel's critical path, so their
+    // waves get issue priority over co-resident shorter items.  Single-kernel plan
+    // (one or two rounds): equal priority, or the short items of the
+    // last-dispatched workgroups, which also take the second round, fall behind
+    // the longest item.
+    if (kFused)
+      __builtin_amdgcn_s_setprio(0);
+    else if (qt >= 1 && 2 * qt >= qt_max)
       __builtin_amdgcn_s_setprio(3);
     else if (qt >= 1 && 4 * qt >= qt_max)
       __builtin_amdgcn_s_setprio(2);
