@@ -19,9 +19,12 @@ SOURCES = [os.path.join(CSRC, "vlca_kernels.hip"), os.path.join(CSRC, "vlca_api.
 
 # Packed fp32 VALU forms are disabled for all device code.  MFMA results are kept
 # in VGPRs (not AGPRs): the softmax reads every score and rescales the
-# accumulators, and AGPR results would need a v_accvgpr copy each way.
+# accumulators, and AGPR results would need a v_accvgpr copy each way.  The
+# atomic optimizer is off: it rewrites the attention kernel's one-lane work
+# claim into a wave-aggregated atomic whose result is waited for at once, which
+# would put the claim's round trip at the start of every item.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def hipcc() -> str:

@@ -12,11 +12,13 @@
 //  * schedule_kernel -- one workgroup turns cu_seqlens into a compact worklist of
 //    (user, q_tile) items, longest first, so no workgroup is launched for rows
 //    that do not exist (the page's dense grid relied on early exit instead).
-//  * attention_kernel -- a persistent grid; work index w maps to item w / H and
-//    head w % H.  With H = 8 and a grid that is a multiple of 8, a workgroup on
-//    XCD x (workgroups are dealt to the 8 XCDs round-robin) always runs head x,
-//    so each XCD's L2 holds one head's K/V columns and serves the re-reads of
-//    later q-tiles of the same user.
+//  * attention_kernel -- a persistent grid over (item, head) pairs.  With H = 8
+//    and a grid that is a multiple of 8, a workgroup on XCD x (workgroups are
+//    dealt to the 8 XCDs round-robin) always runs head x, so each XCD's L2 holds
+//    one head's K/V columns and serves the re-reads of later q-tiles of the same
+//    user.  After the scheduler kernel, workgroups claim items from one counter
+//    per head; in the single-kernel plan (and over a caller's worklist) each
+//    workgroup takes a fixed snake over the list.
 //
 // Attention workgroup: 4 waves; wave w owns query rows 16w..16w+15 of the tile.
 //  * K and V tiles (64 keys x 64 dims, 8 KB each) are copied from HBM straight
