@@ -88,7 +88,7 @@ def cpu_baseline(w, budget_s: float):
 
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {r}/gpurun_out/prof/trace -o run -- "
-             "python3 {r}/bench.py --config {c} --steps 200 --warmup 20 --no-cpu-baseline --cold-steps 0",
+             "python3 {r}/bench.py --config {c} --steps 200 --warmup 2000 --no-cpu-baseline --cold-steps 0",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {r}/gpurun_out/prof/fetch -o run -- "
              "python3 {r}/bench.py --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {r}/gpurun_out/prof/write -o run -- "
@@ -206,7 +206,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # 2000 steps of the 6823-token batch are ~20 ms: measured step times settle
+    # only after several ms of sustained load (with 20 warm-up steps the 44000-token
+    # batch read 48.4 us, with 2000 42.7 us).
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = 6823 tokens / 60 users)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

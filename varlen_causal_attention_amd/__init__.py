@@ -96,15 +96,27 @@ def worklist_capacity(num_users: int, max_seqlen: int) -> int:
     return int(cap.value)
 
 
-def _stream_handle(device) -> int:
-    import torch
+_torch = None
 
-    return int(torch.cuda.current_stream(device).cuda_stream)
+
+def _torch_mod():
+    global _torch
+    if _torch is None:
+        import torch
+
+        _torch = torch
+    return _torch
+
+
+def _stream_handle(device) -> int:
+    """Raw handle of torch's current stream on ``device`` (no Stream object is built)."""
+    torch = _torch_mod()
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return torch._C._cuda_getCurrentRawStream(idx)
 
 
 def _check_cu(cu_seqlens):
-    import torch
-
+    torch = _torch_mod()
     if not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be a 1-D device tensor")
     if cu_seqlens.dtype == torch.int64:
@@ -115,8 +127,7 @@ def _check_cu(cu_seqlens):
 
 
 def _check_qkv(qkv, n_heads, head_dim):
-    import torch
-
+    torch = _torch_mod()
     if not qkv.is_cuda or qkv.dtype != torch.bfloat16 or qkv.dim() != 2:
         raise ValueError("qkv must be a 2-D bfloat16 device tensor")
     if qkv.shape[1] != 3 * n_heads * head_dim:
@@ -128,12 +139,12 @@ def _check_qkv(qkv, n_heads, head_dim):
 
 
 def _out_tensor(qkv, n_heads, head_dim, out):
-    import torch
-
+    torch = _torch_mod()
     shape = (qkv.shape[0], n_heads * head_dim)
     if out is None:
         return torch.empty(shape, dtype=torch.bfloat16, device=qkv.device)
-    if tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != qkv.device:
+    if (tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous()
+            or not out.is_cuda or out.get_device() != qkv.get_device()):
         raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {shape} on {qkv.device}")
     return out
 
@@ -164,8 +175,7 @@ def build_worklist(cu_seqlens, max_seqlen: int) -> Tuple["object", "object"]:
     Rows ``items[:count]`` are (user, q_tile, row_start, length) in the scheduler's order;
     later rows are unspecified.
     """
-    import torch
-
+    torch = _torch_mod()
     cu = _check_cu(cu_seqlens)
     cap = worklist_capacity(cu.shape[0] - 1, max_seqlen)
     items = torch.empty((cap, 4), dtype=torch.int32, device=cu.device)
@@ -181,8 +191,7 @@ def build_worklist(cu_seqlens, max_seqlen: int) -> Tuple["object", "object"]:
 def fwd_with_worklist(qkv, cu_seqlens, max_seqlen: int, items, count, n_heads: int = 8, head_dim: int = 64,
                       scale: Optional[float] = None, out=None):
     """Attention kernel alone over a worklist from :func:`build_worklist` (same cu_seqlens/max_seqlen)."""
-    import torch
-
+    torch = _torch_mod()
     _check_qkv(qkv, n_heads, head_dim)
     cu = _check_cu(cu_seqlens)
     if items.dtype != torch.int32 or items.dim() != 2 or items.shape[1] != 4 or not items.is_contiguous():
