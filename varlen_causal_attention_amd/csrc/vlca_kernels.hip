@@ -22,8 +22,8 @@
 //
 // Attention workgroup: 4 waves; wave w owns query rows 16w..16w+15 of the tile.
 //  * K and V tiles (64 keys x 64 dims, 8 KB each) are copied from HBM straight
-//    into LDS with global_load_lds_dwordx4 (no VGPRs, no VALU), through a ring of
-//    kStages buffers, so kStages-1 tiles are in flight while one is consumed.
+//    into LDS with global_load_lds_dwordx4 (no VGPRs, no VALU), through a
+//    two-stage ring, so the next tile is in flight while one is consumed.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16
 //    (A = K rows from LDS, B = Q held in registers): a lane holds 4 keys of one
 //    query per 16x16 block, so the row max is in-lane work plus two cross-lane
