@@ -78,14 +78,21 @@ enum {
  * `stream`.
  * Small batches (num_users <= 256 and num_users*ceil(max_seqlen/64)*n_heads at most
  * 16 items per resident workgroup; varlen_causal_attn_single_kernel() tells) run
- * as one kernel in which every workgroup locates its own items; they use no
- * library buffer and never allocate.  Otherwise the worklist lives
+ * as one kernel in which every workgroup locates its own items.  When every item
+ * of such a batch, with the long ones split, fits in one round of resident
+ * workgroups, the items of more than max(ceil(t/2), 4) key tiles of a user of t
+ * q-tiles run as two key-range parts whose softmax states are merged; the parts
+ * meet in a fixed-size pool (about 38 MB) kept per (device, stream), allocated by
+ * the first such call on a stream (hipMalloc; while the stream is being captured
+ * and has no pool yet, the call runs its items whole instead).  Splitting
+ * depends on the batch's lengths only, not on max_seqlen; split and whole items
+ * agree within rounding.  Larger batches keep their worklist
  * in a library-owned device buffer kept per (device, stream) and grown on demand:
  * the first call on a stream with a larger num_users*ceil(max_seqlen/64) allocates
  * it (hipMalloc) after synchronising that stream, which is not allowed while the
  * stream is being captured (VLCA_ERR_WORKSPACE then -- make one eager call of the
  * same or larger size first).  Two calls that overlap on the same stream cannot
- * happen (stream order); calls on different streams use different workspaces.
+ * happen (stream order); calls on different streams use different buffers.
  *   qkv        device, bf16 [T, 3*n_heads*head_dim] (see Layouts)
  *   cu_seqlens device, int32 [num_users+1]
  *   num_users  number of segments U (>= 0)
@@ -138,8 +145,8 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
 /*
  * Which launch plan varlen_causal_attn_fwd uses on the current device for these
  * sizes: writes 1 to *single_kernel when it runs one kernel that orders its own
- * work (no worklist buffer, never allocates), 0 when it runs the scheduler and
- * the attention kernel over the library workspace.  No device work; queries the
+ * work (no worklist buffer; at most the fixed split-state pool), 0 when it runs
+ * the scheduler and the attention kernel over the library workspace.  No device work; queries the
  * device's CU count and the kernel's occupancy once.  Errors as for the size
  * checks of varlen_causal_attn_fwd (VLCA_ERR_HIP without a device).
  */

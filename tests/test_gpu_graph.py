@@ -1,7 +1,9 @@
-"""fwd captured in a HIP graph (torch.cuda.CUDAGraph) and replayed: every replay,
-with eager work and synchronisations in between, must reproduce the eager
-output bit for bit.  Covers the single-kernel path (no worklist buffer) and the
-scheduler + worklist path (its buffer exists before capture)."""
+"""fwd captured in a HIP graph (torch.cuda.CUDAGraph) and replayed, and fwd on
+several streams at once.  Every replay, with eager work and synchronisations in
+between, must reproduce the eager output bit for bit; so must every call on a
+stream that runs at the same time as another.  Covers the single-kernel path
+(its split-state pool exists before capture) and the scheduler + worklist path
+(its buffer exists before capture)."""
 import pytest
 import torch
 
@@ -53,6 +55,35 @@ def test_concurrent_streams_match_sequential(gpu):
     wa = workloads.make_config(3)
     wb = workloads.make_from_lengths(list(range(1, 400)), seed=12)
     say(f"[case] concurrent fwd on two streams: {wa.name} and {wb.total_tokens} tokens over {wb.num_users} users")
+    ga, gb = to_gpu(wa), to_gpu(wb)
+    ref_a = vlca.fwd(ga[0], ga[1], wa.max_seqlen, scale=wa.scale)
+    ref_b = vlca.fwd(gb[0], gb[1], wb.max_seqlen, scale=wb.scale)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a, outs_b = [], []
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    for _ in range(8):
+        with torch.cuda.stream(sa):
+            outs_a.append(vlca.fwd(ga[0], ga[1], wa.max_seqlen, scale=wa.scale))
+        with torch.cuda.stream(sb):
+            outs_b.append(vlca.fwd(gb[0], gb[1], wb.max_seqlen, scale=wb.scale))
+    torch.cuda.synchronize()
+    for o in outs_a:
+        assert torch.equal(o, ref_a)
+    for o in outs_b:
+        assert torch.equal(o, ref_b)
+
+
+def test_concurrent_streams_single_kernel_split(gpu):
+    """The same on the single-kernel plan with long items split into key-range
+    parts: each stream has its own pool of part states and arrival counters, and
+    every call leaves the counters ready for the next."""
+    wa = workloads.make_config(2)
+    wb = workloads.make_from_lengths([1000, 700, 3, 450, 0, 320], seed=13)
+    for w in (wa, wb):
+        assert vlca.single_kernel(w.num_users, w.max_seqlen, w.n_heads)
+    say(f"[case] concurrent split single-kernel fwd on two streams: {wa.name} and lengths {list(wb.lengths)}")
     ga, gb = to_gpu(wa), to_gpu(wb)
     ref_a = vlca.fwd(ga[0], ga[1], wa.max_seqlen, scale=wa.scale)
     ref_b = vlca.fwd(gb[0], gb[1], wb.max_seqlen, scale=wb.scale)

@@ -26,6 +26,14 @@ SMALL_CASES = {
     "sixteen_heads": dict(lengths=[33, 190], n_heads=16),
     "all_length_one": dict(lengths=[1] * 50),
     "scaled_values_x4": dict(lengths=[90, 17], value_scale=4.0),
+    # Users of more than 4 q-tiles have their longest items split into key-range
+    # parts that merge their softmax states (single-kernel plan, when the split
+    # list fits in one round of the grid, as in all of these).
+    "split_widths_5_to_16_tiles": dict(lengths=[320, 321, 384, 0, 448, 449, 5, 512, 1000, 257]),
+    "split_one_head_2000": dict(lengths=[2000], n_heads=1),
+    "split_three_heads": dict(lengths=[700, 12, 300], n_heads=3),
+    "split_sixteen_heads": dict(lengths=[1000, 1000], n_heads=16),
+    "split_scaled_values_x4": dict(lengths=[600, 33], value_scale=4.0),
 }
 
 

@@ -1,6 +1,6 @@
 // C ABI of the varlen causal attention library: argument checks (all on the
-// host, before any HIP call), the per-(device, stream) scheduler workspace, and
-// the launches.  Declarations and the full contract are in
+// host, before any HIP call), the per-(device, stream) scheduler workspace and
+// split-state pool, and the launches.  Declarations and the full contract are in
 // include/varlen_causal_attn.h.
 #include <hip/hip_runtime.h>
 
@@ -25,8 +25,24 @@ struct Workspace {
   int64_t capacity = 0;
 };
 
+// Key-range splitting in the single-kernel plan: an item of a user of t q-tiles
+// with more than max(ceil(t / 2), kSplitMinWidth) key tiles runs as two parts on
+// different workgroups, when the batch's split list fits in one round of the
+// grid (the kernel decides from the batch's own lengths).  The parts' softmax
+// states meet in a pool of kPoolSlots slots per (device, stream), shared by the
+// heads.
+constexpr int kSplitParts = vlca::kMaxSplitParts;
+constexpr int kSplitMinWidth = 4;
+constexpr int kPoolSlots = 2048;
+
+struct SplitPool {
+  float* pool = nullptr;    // kPoolSlots slots of kPoolSlotFloats floats
+  int32_t* ctr = nullptr;   // kPoolSlots arrival counters, kSplitCtrStride apart
+};
+
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
+std::map<std::pair<int, hipStream_t>, SplitPool> g_pools;
 std::map<int, int> g_resident;  // 2*device + fused -> resident attention workgroups
 
 int64_t max_tiles_of(int max_seqlen) { return (static_cast<int64_t>(max_seqlen) + vlca::kTileRows - 1) / vlca::kTileRows; }
@@ -69,14 +85,19 @@ int resident_blocks(int dev, bool fused) {
   return r;
 }
 
-int grid_size(int dev, int num_users, int max_seqlen, int n_heads, bool fused) {
+// Persistent grid for `work` (unit, head) pairs: the resident workgroups, capped
+// by the work.
+int grid_size(int dev, int64_t work, bool fused) {
   int64_t g = resident_blocks(dev, fused);
   if (g > vlca::kMaxGrid) g = vlca::kMaxGrid;
   g -= g % 8;  // keeps w % 8 == blockIdx.x % 8 (one head per XCD when H = 8)
   if (g < 8) g = 8;
-  const int64_t work = static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen) * n_heads;
   if (work < g) g = work;
   return static_cast<int>(g);
+}
+
+int64_t item_pairs(int num_users, int max_seqlen, int n_heads) {
+  return static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen) * n_heads;
 }
 
 // Workspace for (device, stream), grown when a call needs more items.  Growth
@@ -109,6 +130,37 @@ int get_workspace(int dev, hipStream_t stream, int64_t capacity, Workspace** out
 
 int32_t* workspace_count(const Workspace* ws) { return reinterpret_cast<int32_t*>(ws->items + ws->capacity); }
 
+// Split-state pool for (device, stream), allocated by the first call that splits
+// (fixed size, never grown); its counters are zeroed in stream order before that
+// call and every call leaves them zero.  *capturing = true (and no pool) when it
+// does not exist yet and the stream is being captured: that call runs unsplit.
+int get_split_pool(int dev, hipStream_t stream, SplitPool** out, bool* capturing) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  *capturing = false;
+  SplitPool& sp = g_pools[std::make_pair(dev, stream)];
+  if (sp.pool == nullptr) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return VLCA_ERR_HIP;
+    if (st != hipStreamCaptureStatusNone) {
+      *capturing = true;
+      return VLCA_OK;
+    }
+    const size_t pool_bytes = static_cast<size_t>(kPoolSlots) * vlca::kPoolSlotFloats * sizeof(float);
+    const size_t ctr_bytes = static_cast<size_t>(kPoolSlots) * vlca::kSplitCtrStride * sizeof(int32_t);
+    void* p = nullptr;
+    if (hipMalloc(&p, pool_bytes + ctr_bytes) != hipSuccess) return VLCA_ERR_WORKSPACE;
+    int32_t* ctr = reinterpret_cast<int32_t*>(static_cast<char*>(p) + pool_bytes);
+    if (hipMemsetAsync(ctr, 0, ctr_bytes, stream) != hipSuccess) {
+      (void)hipFree(p);
+      return VLCA_ERR_HIP;
+    }
+    sp.pool = static_cast<float*>(p);
+    sp.ctr = ctr;
+  }
+  *out = &sp;
+  return VLCA_OK;
+}
+
 // Scheduler (when schedule) then attention.  queue: the library workspace's work
 // counters (dynamic assignment, zeroed by the scheduler), or null for a caller's
 // worklist (fixed assignment).
@@ -121,7 +173,7 @@ int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int m
     if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items, count, queue, stream) != hipSuccess)
       return VLCA_ERR_HIP;
   }
-  const int grid = grid_size(dev, num_users, max_seqlen, n_heads, false);
+  const int grid = grid_size(dev, item_pairs(num_users, max_seqlen, n_heads), false);
   if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
@@ -140,10 +192,25 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   // Small batches: one kernel that locates its own work (no worklist buffer).
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
-  const int grid = grid_size(dev, num_users, max_seqlen, n_heads, true);
+  const int64_t pairs = item_pairs(num_users, max_seqlen, n_heads);
+  int grid = grid_size(dev, pairs, true);
   if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
-    if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, out, grid,
-                                     stream) != hipSuccess)
+    vlca::SplitArgs split{0, 0, 0, nullptr, nullptr};
+    const int cap = kPoolSlots / n_heads;
+    // Only users of more than kSplitMinWidth q-tiles have split items; the kernel
+    // splits them when the whole split list fits in one round of this grid.
+    if (max_tiles > kSplitMinWidth && cap >= kSplitParts) {
+      SplitPool* sp = nullptr;
+      bool capturing = false;
+      rc = get_split_pool(dev, stream, &sp, &capturing);
+      if (rc != VLCA_OK) return rc;
+      if (!capturing) {
+        split = vlca::SplitArgs{kSplitParts, kSplitMinWidth, cap, sp->pool, sp->ctr};
+        grid = grid_size(dev, pairs * kSplitParts, true);
+      }
+    }
+    if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, split, out,
+                                     grid, stream) != hipSuccess)
       return VLCA_ERR_HIP;
     return VLCA_OK;
   }
@@ -198,7 +265,7 @@ int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads,
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
-  const int grid = grid_size(dev, num_users, max_seqlen, n_heads, true);
+  const int grid = grid_size(dev, item_pairs(num_users, max_seqlen, n_heads), true);
   *single_kernel = (num_users > 0 && max_seqlen > 0 && vlca::fused_fits(num_users, max_tiles, n_heads, grid)) ? 1 : 0;
   return VLCA_OK;
 }

@@ -18,6 +18,22 @@ constexpr int kMaxGrid = 4096;       // persistent grid cap
 constexpr int kQueues = 8;
 constexpr int kQueueStride = 64;
 
+// Key-range splitting of long items in the single-kernel plan: an item runs as
+// at most kMaxSplitParts parts; each part leaves its softmax state in a pool slot
+// of kPoolSlotFloats floats; one arrival counter per split item, kSplitCtrStride
+// int32 apart, is zero between calls (the last part resets it).
+constexpr int kMaxSplitParts = 2;
+constexpr int kPoolSlotFloats = 4608;  // O: 64 rows x 64 dims, then (m, l) per thread
+constexpr int kSplitCtrStride = 16;
+
+struct SplitArgs {
+  int p;          // 2: split long items in two parts; <= 1: no splitting
+  int min_width;  // items of at most this many key tiles always run whole
+  int cap;        // pool slots per head: items whose parts' split ranks reach it run whole
+  float* pool;    // [cap][n_heads] slots
+  int32_t* ctr;   // [cap][n_heads] arrival counters
+};
+
 // Scheduler: one workgroup builds the (user, q_tile, row_start, length) list and,
 // when queue is not null, zeroes the kQueues counters at queue.
 hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles,
@@ -30,9 +46,11 @@ hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* c
                             float scale_log2e, void* out, int grid, hipStream_t stream);
 
 // Attention alone with the ordering done inside the kernel (no worklist buffer):
-// for batches where fused_fits() holds.
+// for batches where fused_fits() holds.  split.p == 2 splits long items (needs
+// split.pool / split.ctr).
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
-                                  int n_heads, float scale_log2e, void* out, int grid, hipStream_t stream);
+                                  int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
+                                  hipStream_t stream);
 bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid);
 
 // Attention workgroups that fit on one CU at once (occupancy of the current device),

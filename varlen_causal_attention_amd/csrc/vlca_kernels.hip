@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "vlca_internal.h"
 
 namespace vlca {
@@ -372,9 +374,11 @@ struct Acc {
 
 // One key tile of one item: S^T = K Q^T, mask (diagonal tile only), softmax
 // update, O^T += V^T P^T and l += 1^T P^T.
+// kDiag: keys kk > lim are masked (lim = the lane's query row on the diagonal
+// tile; 63 or more masks nothing).
 template <bool kDiag>
 __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2],
-                                          const bf16x8& ones, float sl2, float rescale_thr, Acc& A) {
+                                          const bf16x8& ones, float sl2, float rescale_thr, Acc& A, int lim = 0) {
   f32x4 s[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -383,12 +387,12 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[b], 0, 0, 0);
   }
-  if (kDiag) {  // key kk visible to query qr iff kk <= qr
+  if (kDiag) {  // key kk visible iff kk <= lim (on the diagonal tile, lim = qr)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (16 * b + 4 * L.g + r > L.qr) s[b][r] = -__builtin_inff();
+        if (16 * b + 4 * L.g + r > lim) s[b][r] = -__builtin_inff();
   }
   // The tile is taken in two halves of 32 keys (score blocks 2hh, 2hh+1), so the
   // second half's QK^T MFMAs run while the first half's softmax is computed.
@@ -443,21 +447,152 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Rounds a workgroup can run when it orders the work itself (kFused), and the
-// most users that path takes (one per thread).
+// most users that path takes (one per thread).  The launch condition counts
+// whole items (kFusedRounds rounds); key-range splitting (below) turns an item
+// into at most kMaxSplitParts work units, so the descriptors hold that many more.
 constexpr int kFusedRounds = 16;
 constexpr int kFusedUsers = kAttnThreads;
+constexpr int kDescRounds = kFusedRounds * kMaxSplitParts;
+
+// ------------------------------------------------------ key-range splitting
+// In the single-kernel plan the longest items bound the kernel: one item walks
+// all of its user's key tiles up to the diagonal.  Such an item can instead run
+// as parts over disjoint key-tile ranges on different workgroups, each part
+// keeping its own (m, l, O) online-softmax state; the state of a softmax over a
+// union of key sets is the rescaled sum of the states over the parts, so the
+// last part to finish folds the others' states into its own and writes the row.
+//
+// Split width of a user of t q-tiles: c = max(ceil(t / 2), min_width) key tiles
+// (0 = no splitting).  Its items with nk > c key tiles (the last t - c q-tiles)
+// run as two parts, key tiles [0, nk/2) and [nk/2, nk) (the diagonal tile in the
+// second); the rest run whole.  The rule depends on the user's own length only.
+// The user's run of work units: the two parts of each split item, q-tiles
+// descending, then its whole items, q-tiles descending.
+struct SplitUser {
+  int c;      // split width (0: no splitting)
+  int split;  // split items: max(t - c, 0)
+};
+
+__device__ __forceinline__ SplitUser split_user(int t, int on, int min_width) {
+  SplitUser r{0, 0};
+  if (on && t > 0) {
+    const int half = (t + 1) >> 1;
+    r.c = half > min_width ? half : min_width;
+    r.split = t > r.c ? t - r.c : 0;
+  }
+  return r;
+}
+
+// Unit i of the run of a user of t q-tiles: its item has nk key tiles and it is
+// part k of p (p = 1: the whole item).
+__device__ __forceinline__ void unit_of(int t, const SplitUser& su, int i, int& nk, int& k, int& p) {
+  if (i < 2 * su.split) {
+    nk = t - (i >> 1);
+    k = i & 1;
+    p = 2;
+  } else {
+    nk = t - su.split - (i - 2 * su.split);
+    k = 0;
+    p = 1;
+  }
+}
+
+// Each part's state goes to a pool slot in global memory, [wave][d][half][lane]
+// float2 for O (4096 floats) then (m, l) per thread (512 floats).  The parts of
+// one item run on different workgroups and possibly different XCDs, whose L2
+// caches are not coherent with each other.  The slots are therefore written and
+// read with agent-scope relaxed atomic accesses, which go through to the
+// device-coherent level, and ordered by waiting for the stores' completion
+// before the arrival count and by reading only after the count has returned.
+// An agent-scope fence would do the same by writing back and invalidating the
+// whole L2 of the XCD, which costs far more with many parts in flight.
+__device__ __forceinline__ void store_coherent(float* p, f32x2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x2 load_coherent(const float* p) {
+  return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Float offset of a lane's O registers (dims 16d + 4g + 0..1; + 128 for + 2..3)
+// inside a pool slot.
+__device__ __forceinline__ int slot_o_offset(const Lanes& L, int d) { return ((L.wid * 4 + d) * 128 + L.lane) * 2; }
+
+// This part's state into its pool slot.
+__device__ __forceinline__ void store_partial(float* slot, const Lanes& L, const Acc& A) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    float* const o = slot + slot_o_offset(L, d);
+    store_coherent(o, f32x2{A.o[d][0], A.o[d][1]});
+    store_coherent(o + 128, f32x2{A.o[d][2], A.o[d][3]});
+  }
+  store_coherent(slot + 4096 + 2 * threadIdx.x, f32x2{A.m, A.l[0]});
+}
+
+// Run by the last part to finish: fold the states of parts 0 .. parts-1 in that
+// order (its own from registers, the others from their slots, slot_stride floats
+// apart), so the result does not depend on which part finished last.
+__device__ __forceinline__ void merge_parts(const float* slot0, int64_t slot_stride, int parts, int part,
+                                            const Lanes& L, float sl2, Acc& A) {
+  float cm = 0.f, cl = 0.f;
+  f32x4 co[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) co[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < parts; ++k) {
+    float xm, xl;
+    f32x4 xo[4];
+    if (k == part) {
+      xm = A.m;
+      xl = A.l[0];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) xo[d] = A.o[d];
+    } else {
+      const float* const s = slot0 + k * slot_stride;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const f32x2 a = load_coherent(s + slot_o_offset(L, d));
+        const f32x2 b = load_coherent(s + slot_o_offset(L, d) + 128);
+        xo[d] = f32x4{a[0], a[1], b[0], b[1]};
+      }
+      const f32x2 ml = load_coherent(s + 4096 + 2 * threadIdx.x);
+      xm = ml[0];
+      xl = ml[1];
+    }
+    if (k == 0) {
+      cm = xm;
+      cl = xl;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) co[d] = xo[d];
+    } else {
+      const float mn = fmaxf(cm, xm);
+      const float a = __builtin_amdgcn_exp2f((cm - mn) * sl2);
+      const float b = __builtin_amdgcn_exp2f((xm - mn) * sl2);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) co[d] = co[d] * a + xo[d] * b;
+      cl = cl * a + xl * b;
+      cm = mn;
+    }
+  }
+  A.m = cm;
+  A.l[0] = cl;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) A.o[d] = co[d];
+}
 
 // kFused = false: walk the first *count items of a worklist built by
-// schedule_kernel.  kFused = true: every workgroup first locates its own items in
-// the same order from cu_seqlens (only for batches with at most kFusedUsers users
-// and kFusedRounds rounds) and keeps their descriptors.
+// schedule_kernel.  kFused = true: every workgroup first locates its own work
+// units in the same order from cu_seqlens (only for batches with at most
+// kFusedUsers users and kFusedRounds rounds of whole items) and keeps their
+// descriptors; with sp.p > 1 the long items run as key-range parts.
 template <bool kFused>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                                  const int4* __restrict__ items,
                                                                  const int32_t* __restrict__ count,
                                                                  int32_t* __restrict__ queue,
                                                                  const int32_t* __restrict__ cu, int U, int max_tiles,
-                                                                 int n_heads, float sl2,
+                                                                 int n_heads, float sl2, SplitArgs sp,
                                                                  uint16_t* __restrict__ out) {
   // Two ring stages (K tile then V tile); tile j of an item lives in stage j%2.
   // The key loop is unrolled by two so that every LDS address is a per-lane
@@ -491,6 +626,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   const int G = gridDim.x;
   const bool by_head = G % n_heads == 0;
   const int slots = by_head ? G / n_heads : G;
+  const int units_per_round = G / n_heads;  // (unit, head) pairs of one round / n_heads
   const int slot = by_head ? blockIdx.x / n_heads : blockIdx.x;
   const int head0 = by_head ? blockIdx.x - slot * n_heads : 0;
   auto work_of = [&](int round, int& item, int& h) {
@@ -505,19 +641,23 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     }
   };
 
-  // kFused: this workgroup's descriptors (q_tile, row_start, length, head), q_tile
-  // < 0 past its last round.
-  __shared__ i32x4 s_desc[kFused ? kFusedRounds : 1];
-  __shared__ int s_qtmax;
+  // kFused: this workgroup's unit descriptors (q_tile | kind << 16, row_start,
+  // length, head | split rank of part 0 << 16), negative past its last round.
+  // kind: 0 the whole item, 1 / 2 its first / second key-range part, 3 nothing
+  // (a first part whose item runs whole as the second).
+  __shared__ i32x4 s_desc[kFused ? kDescRounds : 1];
+  __shared__ int s_arrived;
   int nitems = 0, qt_max = 0;
   if constexpr (kFused) {
     // One user per thread.  Each wave finds, per length class present, the
-    // exclusive prefix of its users' q-tile counts (the same order as the
+    // exclusive prefix of its users' unit counts (the same order as the
     // scheduler kernel: classes descending, users ascending, q-tiles of a user
-    // adjacent and descending); per-wave class sums go through LDS; every wave
-    // then forms the class bases itself, so the slot range of each user is known
-    // in registers.  The item of round r is found by a ballot over "my range
-    // holds it".
+    // adjacent and descending, the parts of a split item adjacent); per-wave
+    // class sums go through LDS; every wave then forms the class bases itself,
+    // so the unit range of each user is known in registers.  The unit of round r
+    // is found by the lane whose range holds it.  Twice the difference of the two
+    // prefixes (with and without splitting) counts the split parts before a
+    // user: the split rank that names a part's pool slot.
     LDS int* const s_wsum = (LDS int*)st0;  // [kWaves][kClasses]
     const int tid = threadIdx.x;
     const int lane = L.lane;
@@ -528,13 +668,17 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     if (tid < nusers) sg = segment_of(cu, cu, false, tid, total, max_tiles);
     const int t = sg.tiles;
     const int cl = t > 0 ? length_class(t) : -1;
+    // The scans sum whole items (low 15 bits) and the units with split items
+    // (high 17 bits) at once; which list is used is decided from the totals.
+    SplitUser spl = split_user(t, sp.p > 1, sp.min_width);
+    const int packed = t | ((t + spl.split) << 15);
     if (lane < kClasses) s_wsum[wid * kClasses + lane] = 0;
     int pre = 0;
     unsigned long long pending = __ballot(t > 0);
     while (pending) {
       const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
       const bool mine = cl == lc;
-      const int x = mine ? t : 0;
+      const int x = mine ? packed : 0;
       const int incl = wave_inclusive_sum(x);
       if (mine) pre = incl - x;
       if (lane == 63) s_wsum[wid * kClasses + lc] = incl;
@@ -548,7 +692,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       for (int w = 0; w < kWaves; ++w) tot += s_wsum[w * kClasses + kClasses - 1 - lane];
     }
     const int incl = wave_inclusive_sum(tot);
-    const int n = __builtin_amdgcn_readlane(incl, kClasses - 1);
+    const int n_both = __builtin_amdgcn_readlane(incl, kClasses - 1);
+    const int n_whole = n_both & 0x7fff, n_split = n_both >> 15;
+    // Split only when every unit of the split list gets a workgroup of its own:
+    // then all parts start at once and none waits for a second round.
+    const bool split = n_split > n_whole && n_split <= units_per_round;
+    const int n = split ? n_split : n_whole;
+    if (!split) spl = SplitUser{0, 0};
+    const int su = t + spl.split;  // work units of this user
     {  // a workgroup past the last item (the grid may exceed the work) leaves now
       int item0, h0;
       work_of(0, item0, h0);
@@ -558,28 +709,53 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     // Every lane takes part in the permute (a lane reads the base of its class
     // from the lane that holds that class).
     const int cbase = __builtin_amdgcn_ds_bpermute(4 * (kClasses - 1 - (t > 0 ? cl : 0)), base);
-    int off = 0;
+    int both = 0;
     if (t > 0) {
-      off = cbase + pre;
-      for (int w = 0; w < wid; ++w) off += s_wsum[w * kClasses + cl];
+      both = cbase + pre;
+      for (int w = 0; w < wid; ++w) both += s_wsum[w * kClasses + cl];
     }
-    // Items of later rounds lie further down the list, so the first round past
-    // the end closes this workgroup's descriptors.
-    for (int r = 0; r < kFusedRounds; ++r) {
-      int item, h;
-      work_of(r, item, h);
-      if (item >= n) {
-        if (tid == 0) s_desc[r] = i32x4{-1, 0, 0, 0};
-        break;
+    // The user's first unit, and the split rank of its first split part (two per
+    // split item of the users before it).
+    const int off = split ? both >> 15 : both & 0x7fff;
+    const int roff = 2 * ((both >> 15) - (both & 0x7fff));
+    // Units of later rounds lie further down the list, so the first round past
+    // the end closes this workgroup's descriptors.  (The list without split
+    // items has its own copy of the loop: it is on every batch's critical path.)
+    auto fill = [&](auto with_split) {
+      for (int r = 0; r < kDescRounds; ++r) {
+        int item, h;
+        work_of(r, item, h);
+        if (item >= n) {
+          if (tid == 0) s_desc[r] = i32x4{-1, 0, 0, 0};
+          break;
+        }
+        if (t > 0 && item >= off && item < off + su) {
+          const int i = item - off;
+          if constexpr (decltype(with_split)::value) {
+            int nk, k, p;
+            unit_of(t, spl, i, nk, k, p);
+            int kind = 0, rank0 = 0;
+            if (p > 1) {
+              const int r0 = roff + i - k;  // split ranks r0, r0+1
+              if (r0 + 2 <= sp.cap) {
+                kind = 1 + k;
+                rank0 = r0;
+              } else if (k == 0) {
+                kind = 3;  // pool full: the second part runs the whole item, the first nothing
+              }
+            }
+            s_desc[r] = i32x4{(nk - 1) | (kind << 16), sg.start, sg.len, h | (rank0 << 16)};
+          } else {
+            s_desc[r] = i32x4{t - 1 - i, sg.start, sg.len, h};
+          }
+        }
       }
-      if (t > 0 && item >= off && item < off + t) s_desc[r] = i32x4{t - 1 - (item - off), sg.start, sg.len, h};
-    }
-    // The first item (slot 0) is the last q-tile of the first user of the top class.
-    const unsigned long long first = __ballot(t > 0 && off == 0);
-    if (first && lane == __builtin_ctzll(first)) s_qtmax = t - 1;
-    if (tid == 0 && n == 0) s_qtmax = 0;
+    };
+    if (split)
+      fill(std::true_type{});
+    else
+      fill(std::false_type{});
     lds_barrier();  // descriptors visible; the ring is free again
-    qt_max = s_qtmax;
   } else {
     nitems = *count;
     qt_max = nitems > 0 ? items[0].y : 0;  // the first item is a longest user's last q-tile
@@ -604,14 +780,31 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   }
   for (int round = 0;; ++round) {
     int qt, start, len, h;
+    // Key tiles [klo, khi) of the item; a split item's part `part` of `parts`,
+    // whose state goes to pool slot rank0 + part (split ranks of this head).
+    int klo = 0, khi, parts = 1, rank0 = 0, part = 0;
     if constexpr (kFused) {
-      if (round >= kFusedRounds) break;
+      if (round >= kDescRounds) break;
       const i32x4 d = s_desc[round];
-      qt = __builtin_amdgcn_readfirstlane(d[0]);
-      if (qt < 0) break;
+      const int w0 = __builtin_amdgcn_readfirstlane(d[0]);
+      if (w0 < 0) break;
       start = __builtin_amdgcn_readfirstlane(d[1]);
       len = __builtin_amdgcn_readfirstlane(d[2]);
-      h = __builtin_amdgcn_readfirstlane(d[3]);
+      const int w3 = __builtin_amdgcn_readfirstlane(d[3]);
+      qt = w0 & 0xffff;
+      h = w3 & 0xffff;
+      const int kind = w0 >> 16;
+      if (kind == 3) continue;  // its item runs whole as the second part
+      khi = qt + 1;
+      if (kind != 0) {  // key tiles [0, nk/2) or [nk/2, nk)
+        parts = 2;
+        part = kind - 1;
+        rank0 = w3 >> 16;
+        if (part == 0)
+          khi >>= 1;
+        else
+          klo = khi >> 1;
+      }
     } else {
       int item;
       if (dyn) {
@@ -633,6 +826,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       qt = it.y;
       start = it.z;
       len = it.w;
+      khi = qt + 1;
     }
     const int q0 = qt * kTileRows;
     const int lim = len - 1 - q0;  // the user's last row, relative to the diagonal tile
@@ -688,8 +882,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
         copy_to_lds(qg, (uint32_t)(r * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i]))), m0 + kStageBytes + 1024 * i);
       }
     }
-    issue_tile(0, 0);
-    wait_vmem_lds<4>();  // this wave's Q rows have landed (tile 0's 4 copies may be in flight)
+    issue_tile(0, klo);
+    wait_vmem_lds<4>();  // this wave's Q rows have landed (the first tile's 4 copies may be in flight)
     bf16x8 qf[2];
     qf[0] = lds_b128(st1, L.qr * 128 + ((L.g ^ swz(L.qr)) << 4));
     qf[1] = lds_b128(st1, L.qr * 128 + (((4 + L.g) ^ swz(L.qr)) << 4));
@@ -705,9 +899,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     // Before consuming tile j: wait for this wave's copies of it, then a barrier
     // makes every wave's copies visible and guarantees that the other stage (tile
     // j-1, or the Q rows) has been read by every wave, so tile j+1 may refill it.
-    // Off-diagonal tiles (j < qt) need no mask; the diagonal tile runs last.
-    int j = 0;
-    for (; j + 2 <= qt; j += 2) {
+    // Tile j of the range sits in stage (j - klo) % 2.  Only the diagonal tile
+    // (qt, the last tile of the range when khi == qt + 1) needs a mask; the last
+    // tile of a first part goes through the same masked step with nothing masked.
+    const int mlim = (!kFused || khi == qt + 1) ? L.qr : kTileRows - 1;
+    int j = klo;
+    for (; j + 2 < khi; j += 2) {
       wait_and_barrier<0>();
       issue_tile(kStageBytes, j + 1);
       tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
@@ -715,20 +912,40 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       issue_tile(0, j + 2);
       tile_step<false>(st1, L, qf, ones, sl2, rescale_thr, A);
     }
-    if (j < qt) {  // qt odd: tile qt-1 in stage 0, the diagonal tile goes to stage 1
+    if (j + 1 < khi) {  // two tiles left: j in stage 0, the last one goes to stage 1
       wait_and_barrier<0>();
-      issue_tile(kStageBytes, qt);
+      issue_tile(kStageBytes, j + 1);
       tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
       wait_and_barrier<0>();
-      tile_step<true>(st1, L, qf, ones, sl2, rescale_thr, A);
-    } else {  // qt even: the diagonal tile is in stage 0
+      tile_step<true>(st1, L, qf, ones, sl2, rescale_thr, A, mlim);
+    } else {  // one tile left, in stage 0
       wait_and_barrier<0>();
-      tile_step<true>(st0, L, qf, ones, sl2, rescale_thr, A);
+      tile_step<true>(st0, L, qf, ones, sl2, rescale_thr, A, mlim);
     }
     // The claim made at the item's start is passed on; every wave read s_next
     // before this item's first barrier.
     if (dyn && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring before the next item refills it
+
+    if (parts > 1) {
+      // Leave this part's state in its slot; count the arrival once every wave's
+      // stores have completed.  The last part to arrive resets the counter for
+      // the next call and merges; the others are done with this unit.
+      const int64_t slot_stride = (int64_t)n_heads * kPoolSlotFloats;
+      float* const slot0 = sp.pool + (int64_t)rank0 * slot_stride + (int64_t)h * kPoolSlotFloats;
+      store_partial(slot0 + part * slot_stride, L, A);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      if (threadIdx.x == 0) {
+        int32_t* const c = sp.ctr + ((int64_t)rank0 * n_heads + h) * kSplitCtrStride;
+        const int before = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (before == parts - 1) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_arrived = before;
+      }
+      lds_barrier();
+      if (__builtin_amdgcn_readfirstlane(s_arrived) != parts - 1) continue;
+      merge_parts(slot0, slot_stride, parts, part, L, sl2, A);
+    }
 
     if (L.qr < len - q0) {
       const float inv = 1.0f / A.l[0];
@@ -757,20 +974,23 @@ hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* c
                             float scale_log2e, void* out, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(attention_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, scale_log2e,
-                     static_cast<uint16_t*>(out));
+                     SplitArgs{0, 0, 0, nullptr, nullptr}, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
-                                  int n_heads, float scale_log2e, void* out, int grid, hipStream_t stream) {
+                                  int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
+                                  hipStream_t stream) {
   hipLaunchKernelGGL(attention_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(qkv), nullptr, nullptr, nullptr, cu_seqlens, num_users, max_tiles,
-                     n_heads, scale_log2e, static_cast<uint16_t*>(out));
+                     n_heads, scale_log2e, split, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
 bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid) {
   if (num_users > kFusedUsers || grid <= 0) return false;
+  // The prologue's scans carry the item count in 15 bits (and up to twice it in 17).
+  if (num_users * max_tiles > 32767) return false;
   // rounds = ceil(items * H / grid) when the grid is a multiple of H; items <= users x max q-tiles
   return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
