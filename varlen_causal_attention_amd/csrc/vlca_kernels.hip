@@ -641,58 +641,84 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     }
   };
 
-  // kFused: this workgroup's unit descriptors (q_tile | kind << 16, row_start,
-  // length, head | split rank of part 0 << 16), negative past its last round.
+  // kFused: the workgroup's unit descriptors (q_tile | kind << 16, row_start,
+  // length, head | split rank of part 0 << 16), negative past its last round;
+  // shared by the waves, or one copy per wave when each wave orders the users.
   // kind: 0 the whole item, 1 / 2 its first / second key-range part, 3 nothing
   // (a first part whose item runs whole as the second).
-  __shared__ i32x4 s_desc[kFused ? kDescRounds : 1];
+  __shared__ i32x4 s_desc[kFused ? kWaves * kDescRounds : 1];
+  int desc_base = 0;  // this wave's descriptors: s_desc[desc_base + round]
   __shared__ int s_arrived;
   int nitems = 0, qt_max = 0;
   if constexpr (kFused) {
-    // One user per thread.  Each wave finds, per length class present, the
-    // exclusive prefix of its users' unit counts (the same order as the
-    // scheduler kernel: classes descending, users ascending, q-tiles of a user
-    // adjacent and descending, the parts of a split item adjacent); per-wave
-    // class sums go through LDS; every wave then forms the class bases itself,
-    // so the unit range of each user is known in registers.  The unit of round r
-    // is found by the lane whose range holds it.  Twice the difference of the two
-    // prefixes (with and without splitting) counts the split parts before a
-    // user: the split rank that names a part's pool slot.
-    LDS int* const s_wsum = (LDS int*)st0;  // [kWaves][kClasses]
-    const int tid = threadIdx.x;
+    // The unit list: users grouped by length class, classes descending, users
+    // ascending inside a class (the same order as the scheduler kernel); a
+    // user's units adjacent (the two parts of each split item, then its whole
+    // items, q-tiles descending).  A user's first unit is the units of all
+    // higher classes plus those of the users before it in its class.  The scans
+    // sum whole items (low 15 bits) and the units with split items (high 17 bits)
+    // at once; which list runs is decided from the totals, and twice the
+    // difference of the two prefixes counts the split parts before a user (the
+    // split rank that names a part's pool slot).  The unit of round r is found by
+    // the lane whose range holds it.
     const int lane = L.lane;
-    const int wid = L.wid;
     const int nusers = max_tiles > 0 ? U : 0;
     const int total = nusers > 0 ? cu[nusers] : 0;
+    // At most 64 users: every wave orders them by itself (a user per lane), with
+    // no LDS exchange and no barrier, and keeps its own copy of the descriptors.
+    // Otherwise one user per thread, per-wave class sums through LDS.
+    const bool one_wave = nusers <= 64;
+    const int me = one_wave ? lane : threadIdx.x;  // this thread's user
     Seg sg{0, 0, 0};
-    if (tid < nusers) sg = segment_of(cu, cu, false, tid, total, max_tiles);
+    if (me < nusers) sg = segment_of(cu, cu, false, me, total, max_tiles);
     const int t = sg.tiles;
     const int cl = t > 0 ? length_class(t) : -1;
-    // The scans sum whole items (low 15 bits) and the units with split items
-    // (high 17 bits) at once; which list is used is decided from the totals.
     SplitUser spl = split_user(t, sp.p > 1, sp.min_width);
     const int packed = t | ((t + spl.split) << 15);
-    if (lane < kClasses) s_wsum[wid * kClasses + lane] = 0;
-    int pre = 0;
-    unsigned long long pending = __ballot(t > 0);
-    while (pending) {
-      const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
-      const bool mine = cl == lc;
-      const int x = mine ? packed : 0;
-      const int incl = wave_inclusive_sum(x);
-      if (mine) pre = incl - x;
-      if (lane == 63) s_wsum[wid * kClasses + lc] = incl;
-      pending &= ~__ballot(mine);
-    }
-    lds_barrier();
-    // Class totals and bases (lane l handles class 12-l), the user's first slot.
-    int tot = 0;
-    if (lane < kClasses) {
+    int both = 0, n_both = 0;
+    if (one_wave) {
+      // Classes in descending order: the running total is the next class's base.
+      for (int c = kClasses - 1; c >= 0; --c) {
+        const bool mine = cl == c;
+        if (__ballot(mine) == 0) continue;  // uniform
+        const int x = mine ? packed : 0;
+        const int incl = wave_inclusive_sum(x);
+        if (mine) both = n_both + incl - x;
+        n_both += __builtin_amdgcn_readlane(incl, 63);
+      }
+    } else {
+      LDS int* const s_wsum = (LDS int*)st0;  // [kWaves][kClasses]
+      const int wid = L.wid;
+      if (lane < kClasses) s_wsum[wid * kClasses + lane] = 0;
+      int pre = 0;
+      unsigned long long pending = __ballot(t > 0);
+      while (pending) {
+        const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
+        const bool mine = cl == lc;
+        const int x = mine ? packed : 0;
+        const int incl = wave_inclusive_sum(x);
+        if (mine) pre = incl - x;
+        if (lane == 63) s_wsum[wid * kClasses + lc] = incl;
+        pending &= ~__ballot(mine);
+      }
+      lds_barrier();
+      // Class totals and bases (lane l handles class 12-l), the user's first slot.
+      int tot = 0;
+      if (lane < kClasses) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) tot += s_wsum[w * kClasses + kClasses - 1 - lane];
+        for (int w = 0; w < kWaves; ++w) tot += s_wsum[w * kClasses + kClasses - 1 - lane];
+      }
+      const int incl = wave_inclusive_sum(tot);
+      n_both = __builtin_amdgcn_readlane(incl, kClasses - 1);
+      const int base = incl - tot;  // first slot of class 12-lane
+      // Every lane takes part in the permute (a lane reads the base of its class
+      // from the lane that holds that class).
+      const int cbase = __builtin_amdgcn_ds_bpermute(4 * (kClasses - 1 - (t > 0 ? cl : 0)), base);
+      if (t > 0) {
+        both = cbase + pre;
+        for (int w = 0; w < wid; ++w) both += s_wsum[w * kClasses + cl];
+      }
     }
-    const int incl = wave_inclusive_sum(tot);
-    const int n_both = __builtin_amdgcn_readlane(incl, kClasses - 1);
     const int n_whole = n_both & 0x7fff, n_split = n_both >> 15;
     // Split only when every unit of the split list gets a workgroup of its own:
     // then all parts start at once and none waits for a second round.
@@ -705,28 +731,21 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       work_of(0, item0, h0);
       if (item0 >= n) return;  // uniform across the workgroup
     }
-    const int base = incl - tot;  // first slot of class 12-lane
-    // Every lane takes part in the permute (a lane reads the base of its class
-    // from the lane that holds that class).
-    const int cbase = __builtin_amdgcn_ds_bpermute(4 * (kClasses - 1 - (t > 0 ? cl : 0)), base);
-    int both = 0;
-    if (t > 0) {
-      both = cbase + pre;
-      for (int w = 0; w < wid; ++w) both += s_wsum[w * kClasses + cl];
-    }
     // The user's first unit, and the split rank of its first split part (two per
     // split item of the users before it).
     const int off = split ? both >> 15 : both & 0x7fff;
     const int roff = 2 * ((both >> 15) - (both & 0x7fff));
     // Units of later rounds lie further down the list, so the first round past
-    // the end closes this workgroup's descriptors.  (The list without split
-    // items has its own copy of the loop: it is on every batch's critical path.)
+    // the end closes the descriptors.  (The list without split items has its own
+    // copy of the loop: it is on every batch's critical path.)
+    LDS i32x4* const desc = (LDS i32x4*)s_desc + (one_wave ? L.wid * kDescRounds : 0);
+    const bool writer = one_wave ? lane == 0 : threadIdx.x == 0;
     auto fill = [&](auto with_split) {
       for (int r = 0; r < kDescRounds; ++r) {
         int item, h;
         work_of(r, item, h);
         if (item >= n) {
-          if (tid == 0) s_desc[r] = i32x4{-1, 0, 0, 0};
+          if (writer) desc[r] = i32x4{-1, 0, 0, 0};
           break;
         }
         if (t > 0 && item >= off && item < off + su) {
@@ -744,9 +763,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
                 kind = 3;  // pool full: the second part runs the whole item, the first nothing
               }
             }
-            s_desc[r] = i32x4{(nk - 1) | (kind << 16), sg.start, sg.len, h | (rank0 << 16)};
+            desc[r] = i32x4{(nk - 1) | (kind << 16), sg.start, sg.len, h | (rank0 << 16)};
           } else {
-            s_desc[r] = i32x4{t - 1 - i, sg.start, sg.len, h};
+            desc[r] = i32x4{t - 1 - i, sg.start, sg.len, h};
           }
         }
       }
@@ -755,7 +774,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       fill(std::true_type{});
     else
       fill(std::false_type{});
-    lds_barrier();  // descriptors visible; the ring is free again
+    if (one_wave) {
+      // The descriptors came from lanes of this wave: wait for the writes.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      lds_barrier();  // descriptors visible; the ring is free again
+    }
+    desc_base = one_wave ? L.wid * kDescRounds : 0;
   } else {
     nitems = *count;
     qt_max = nitems > 0 ? items[0].y : 0;  // the first item is a longest user's last q-tile
@@ -785,7 +811,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     int klo = 0, khi, parts = 1, rank0 = 0, part = 0;
     if constexpr (kFused) {
       if (round >= kDescRounds) break;
-      const i32x4 d = s_desc[round];
+      const i32x4 d = s_desc[desc_base + round];
       const int w0 = __builtin_amdgcn_readfirstlane(d[0]);
       if (w0 < 0) break;
       start = __builtin_amdgcn_readfirstlane(d[1]);
