@@ -27,7 +27,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 KERNEL_SRC = os.path.join(ROOT, "varlen_causal_attention_amd", "csrc", "vlca_kernels.hip")
-ATTN_KERNEL = "attention_kernel"           # attention_kernel<true>: single-kernel plan; <false>: over a worklist
+ATTN_KERNEL = "attention_kernel"           # <true, true>: single-kernel plan; <false, ...>: over a worklist
 
 
 def kernel_source_hash() -> str:
@@ -162,8 +162,8 @@ def summarize_profiles(root: str, config: int) -> None:
     # HBM traffic: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy's reading,
     # for the attention kernel fwd runs (the single-kernel instance when present).
     fetch_rows = _read_csv(os.path.join(root, "fetch", "run_counter_collection.csv"))
-    kern = f"{ATTN_KERNEL}<true>" if any(f"{ATTN_KERNEL}<true>" in r["Kernel_Name"] for r in fetch_rows) \
-        else f"{ATTN_KERNEL}<false>"
+    kern = f"{ATTN_KERNEL}<true, true>" if any(f"{ATTN_KERNEL}<true, true>" in r["Kernel_Name"] for r in fetch_rows) \
+        else f"{ATTN_KERNEL}<false"
     fetch_kib, n_f = _counter_mean(os.path.join(root, "fetch"), kern, "FETCH_SIZE")
     write_kib, n_w = _counter_mean(os.path.join(root, "write"), kern, "WRITE_SIZE")
     copy_f, _ = _counter_mean(os.path.join(root, "copyf"), COPY_KERNEL, "FETCH_SIZE")
@@ -293,7 +293,7 @@ def main():
     torch.cuda.synchronize()
     ms_worklist_kernel = e0.elapsed_time(e1) / args.steps
     ms_attn = ms_step if single else ms_worklist_kernel
-    kernel_name = f"{ATTN_KERNEL}<{'true' if single else 'false'}>"
+    kernel_name = f"{ATTN_KERNEL}<true, true>" if single else f"{ATTN_KERNEL}<false, ...>"
     print(f"[bench] step {ms_step * 1e3:.2f} us ({'single kernel' if single else 'scheduler + attention'}), "
           f"attention kernel over a worklist {ms_worklist_kernel * 1e3:.2f} us", file=sys.stderr, flush=True)
 

@@ -78,15 +78,16 @@ enum {
  * `stream`.
  * Small batches (num_users <= 256 and num_users*ceil(max_seqlen/64)*n_heads at most
  * 16 items per resident workgroup; varlen_causal_attn_single_kernel() tells) run
- * as one kernel in which every workgroup locates its own items.  When every item
- * of such a batch, with the long ones split, fits in one round of resident
- * workgroups, the items of more than max(ceil(t/2), 4) key tiles of a user of t
- * q-tiles run as two key-range parts whose softmax states are merged; the parts
- * meet in a fixed-size pool (about 38 MB) kept per (device, stream), allocated by
- * the first such call on a stream (hipMalloc; while the stream is being captured
- * and has no pool yet, the call runs its items whole instead).  Splitting
- * depends on the batch's lengths only, not on max_seqlen; split and whole items
- * agree within rounding.  Larger batches keep their worklist
+ * as one kernel in which every workgroup locates its own items.  In a batch of
+ * at most 256 users whose items, with the long ones split, fit in one round of
+ * resident workgroups, the items of more than max(ceil(t/2), 4) key tiles of a
+ * user of t q-tiles run as two key-range parts whose softmax states are merged
+ * (on either plan, with the same decision, so max_seqlen does not change the
+ * bits).  The parts meet in a fixed-size pool (about 38 MB) kept per (device,
+ * stream), allocated by the first call on a stream that may split (hipMalloc;
+ * while the stream is being captured and has no pool yet, the call runs its
+ * items whole instead).  Split and whole items agree within rounding; the
+ * worklist entry points below always run items whole.  Larger batches keep their worklist
  * in a library-owned device buffer kept per (device, stream) and grown on demand:
  * the first call on a stream with a larger num_users*ceil(max_seqlen/64) allocates
  * it (hipMalloc) after synchronising that stream, which is not allowed while the

@@ -62,21 +62,27 @@ def test_isolation_other_users_bit_identical(gpu):
     assert not torch.equal(base[~keep], out[~keep])
 
 
-def test_max_seqlen_invariance(gpu):
-    w = workloads.make_config(2)
-    say("[case] max_seqlen 452 / 1024 / 2048 / 262144")
+# A larger max_seqlen may move a batch from the single-kernel plan to the
+# scheduler plan; both take the same key-range split decision from the batch's
+# own lengths, so the bits stay the same.
+MAX_SEQLEN_CASES = [
+    ("config 2 (no item split)", lambda: workloads.make_config(2), (1024, 2048, 262144)),
+    ("long users, items split", lambda: workloads.make_from_lengths([1000, 700, 3, 450, 0, 320], seed=13),
+     (1024, 4096, 65536, 262144)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MAX_SEQLEN_CASES)))
+def test_max_seqlen_invariance(gpu, case):
+    name, make, larger = MAX_SEQLEN_CASES[case]
+    w = make()
+    say(f"[case] max_seqlen {w.max_seqlen} / {larger}: {name}")
     qkv, cu = to_gpu(w)
     ref = run_fwd(w, qkv=qkv, cu=cu)
-    # The same single-kernel plan: the split of long items depends on each user's
-    # own length only, so the bits do not change.
-    for ms in (1024, 2048):
-        assert vlca.single_kernel(w.num_users, ms, w.n_heads)
+    plans = {vlca.single_kernel(w.num_users, ms, w.n_heads) for ms in (w.max_seqlen,) + larger}
+    assert plans == {True, False}  # both launch plans are covered
+    for ms in larger:
         assert torch.equal(ref, run_fwd(w, max_seqlen=ms, qkv=qkv, cu=cu)), ms
-    # 262144 selects the scheduler plan, whose items run whole: users without split
-    # items give the same bits, the others agree within the parity bound.
-    assert not vlca.single_kernel(w.num_users, 262144, w.n_heads)
-    out = run_fwd(w, max_seqlen=262144, qkv=qkv, cu=cu)
-    assert_same_or_close(ref, out, w)
 
 
 def test_zero_length_users_change_nothing(gpu):
@@ -159,10 +165,11 @@ def test_constant_v(gpu):
 
 # Batches with at most 256 users (and few enough items per workgroup) run as one
 # kernel that locates its own work; larger ones run the scheduler and the
-# attention kernel over a worklist buffer.  The scheduler plan must give the same
-# bits as the explicit worklist path; the single-kernel plan splits the longest
-# items of users of more than 4 q-tiles, whose rows then agree within the parity
-# bound (all other rows bit for bit).
+# attention kernel over a worklist buffer.  For batches of at most 256 users
+# either plan of fwd may split the longest items of users of more than 4 q-tiles
+# into key-range parts, while the explicit worklist path runs every item whole:
+# rows of users that never split agree bit for bit, the others within the parity
+# bound.  Larger batches never split and agree bit for bit.
 WORKLIST_CASES = [
     ("config 2 (single kernel)", lambda: workloads.make_config(2), None),
     ("config 3 (scheduler + worklist)", lambda: workloads.make_config(3), None),
@@ -173,6 +180,8 @@ WORKLIST_CASES = [
     ("zero-length users, 3 heads", lambda: workloads.make_from_lengths([0, 70, 0, 0, 5, 200, 0], seed=5, n_heads=3),
      None),
     ("one user of 4096 rows (64 q-tiles)", lambda: workloads.make_from_lengths([4096], seed=6), None),
+    ("one user of 4096 rows, max_seqlen 262144 (scheduler plan, split)",
+     lambda: workloads.make_from_lengths([4096], seed=6), 262144),
     # Scheduler plan (more than 256 users) with counters that cannot be one per head:
     # 3 heads (the grid is not a multiple of the head count) and 16 heads (more heads
     # than counters) both claim (item, head) pairs from a single counter.
@@ -196,7 +205,7 @@ def test_worklist_entry_point_matches_fwd(gpu, case):
     items, count = vlca.build_worklist(cu, ms)
     b = vlca.fwd_with_worklist(qkv, cu, ms, items, count, n_heads=w.n_heads, scale=w.scale)
     torch.cuda.synchronize()
-    if vlca.single_kernel(w.num_users, ms, w.n_heads):
+    if w.num_users <= 256:
         assert_same_or_close(a, b.cpu(), w)
     else:
         assert torch.equal(a, b.cpu())

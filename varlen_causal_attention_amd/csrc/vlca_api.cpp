@@ -4,6 +4,7 @@
 // include/varlen_causal_attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <map>
@@ -163,18 +164,23 @@ int get_split_pool(int dev, hipStream_t stream, SplitPool** out, bool* capturing
 
 // Scheduler (when schedule) then attention.  queue: the library workspace's work
 // counters (dynamic assignment, zeroed by the scheduler), or null for a caller's
-// worklist (fixed assignment).
+// worklist (fixed assignment).  split: key-range splitting (fwd's scheduler plan
+// only; a caller's worklist always holds whole items).
 int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, float scale,
-                int4* items, int32_t* count, int32_t* queue, void* out, hipStream_t stream, bool schedule) {
+                int4* items, int32_t* count, int32_t* queue, const vlca::SplitArgs& split, void* out,
+                hipStream_t stream, bool schedule) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   if (schedule) {
-    if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items, count, queue, stream) != hipSuccess)
+    if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, items, count, queue, split, stream) != hipSuccess)
       return VLCA_ERR_HIP;
   }
-  const int grid = grid_size(dev, item_pairs(num_users, max_seqlen, n_heads), false);
-  if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, out, grid, stream) != hipSuccess)
+  int64_t pairs = item_pairs(num_users, max_seqlen, n_heads);
+  if (split.p > 1) pairs *= kSplitParts;
+  const int grid = grid_size(dev, pairs, false);
+  if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, split, out, grid, stream) !=
+      hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
@@ -194,31 +200,42 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   const int64_t pairs = item_pairs(num_users, max_seqlen, n_heads);
   int grid = grid_size(dev, pairs, true);
-  if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
-    vlca::SplitArgs split{0, 0, 0, nullptr, nullptr};
-    const int cap = kPoolSlots / n_heads;
-    // Only users of more than kSplitMinWidth q-tiles have split items; the kernel
-    // splits them when the whole split list fits in one round of this grid.
-    if (max_tiles > kSplitMinWidth && cap >= kSplitParts) {
-      SplitPool* sp = nullptr;
-      bool capturing = false;
-      rc = get_split_pool(dev, stream, &sp, &capturing);
-      if (rc != VLCA_OK) return rc;
-      if (!capturing) {
-        split = vlca::SplitArgs{kSplitParts, kSplitMinWidth, cap, sp->pool, sp->ctr};
-        grid = grid_size(dev, pairs * kSplitParts, true);
-      }
+  // Key-range splitting: both plans take the same decision from the batch's own
+  // lengths (split when the list with split items has at most upr units, one
+  // round of the single-kernel grid), so max_seqlen, which picks the plan, does
+  // not change the bits.  Batches of more than kFusedUsers users never split.
+  // Only users of more than kSplitMinWidth q-tiles have split items.
+  vlca::SplitArgs split{0, 0, 0, 0, nullptr, nullptr};
+  const int cap = kPoolSlots / n_heads;
+  if (num_users <= vlca::kFusedUsers && max_tiles > kSplitMinWidth && cap >= kSplitParts) {
+    SplitPool* sp = nullptr;
+    bool capturing = false;
+    rc = get_split_pool(dev, stream, &sp, &capturing);
+    if (rc != VLCA_OK) return rc;
+    if (!capturing) {
+      const int upr = std::max(1, grid_size(dev, INT64_MAX, true) / n_heads);
+      split = vlca::SplitArgs{kSplitParts, kSplitMinWidth, upr, cap, sp->pool, sp->ctr};
     }
+  }
+  if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
+    if (split.p > 1) grid = grid_size(dev, pairs * kSplitParts, true);
     if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, split, out,
                                      grid, stream) != hipSuccess)
       return VLCA_ERR_HIP;
     return VLCA_OK;
   }
+  // The worklist may hold split units: at most upr more than the whole items.
+  const int64_t need = required_capacity(num_users, max_seqlen);
   Workspace* ws = nullptr;
-  rc = get_workspace(dev, stream, required_capacity(num_users, max_seqlen), &ws);
+  rc = get_workspace(dev, stream, split.p > 1 ? need + std::min<int64_t>(need, split.upr) : need, &ws);
+  if (rc == VLCA_ERR_WORKSPACE && split.p > 1) {
+    // E.g. a stream being captured whose workspace only holds whole items: run them whole.
+    split = vlca::SplitArgs{0, 0, 0, 0, nullptr, nullptr};
+    rc = get_workspace(dev, stream, need, &ws);
+  }
   if (rc != VLCA_OK) return rc;
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, ws->items, workspace_count(ws),
-                     workspace_count(ws) + vlca::kQueueStride, out, stream, true);
+                     workspace_count(ws) + vlca::kQueueStride, split, out, stream, true);
 }
 
 int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity) {
@@ -239,7 +256,7 @@ int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, 
   if (capacity < need) return VLCA_ERR_CAPACITY;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, reinterpret_cast<int4*>(items), count, nullptr,
-                            stream) != hipSuccess)
+                            vlca::SplitArgs{0, 0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
@@ -253,8 +270,8 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
   if (num_users > 0 && capacity < required_capacity(num_users, max_seqlen)) return VLCA_ERR_CAPACITY;
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale,
-                     reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), nullptr, out,
-                     stream, false);
+                     reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), nullptr,
+                     vlca::SplitArgs{0, 0, 0, 0, nullptr, nullptr}, out, stream, false);
 }
 
 int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads, int* single_kernel) {

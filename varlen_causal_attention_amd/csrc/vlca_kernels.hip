@@ -104,19 +104,55 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
   return x;
 }
 
+// Split width of a user of t q-tiles: c = max(ceil(t / 2), min_width) key tiles
+// (0 = no splitting).  Its items with nk > c key tiles (the last t - c q-tiles)
+// run as two parts, key tiles [0, nk/2) and [nk/2, nk) (the diagonal tile in the
+// second); the rest run whole.  The rule depends on the user's own length only.
+// The user's run of work units: the two parts of each split item, q-tiles
+// descending, then its whole items, q-tiles descending.
+struct SplitUser {
+  int c;      // split width (0: no splitting)
+  int split;  // split items: max(t - c, 0)
+};
+
+__device__ __forceinline__ SplitUser split_user(int t, int on, int min_width) {
+  SplitUser r{0, 0};
+  if (on && t > 0) {
+    const int half = (t + 1) >> 1;
+    r.c = half > min_width ? half : min_width;
+    r.split = t > r.c ? t - r.c : 0;
+  }
+  return r;
+}
+
+// Unit i of the run of a user of t q-tiles: its item has nk key tiles and it is
+// part k of p (p = 1: the whole item).
+__device__ __forceinline__ void unit_of(int t, const SplitUser& su, int i, int& nk, int& k, int& p) {
+  if (i < 2 * su.split) {
+    nk = t - (i >> 1);
+    k = i & 1;
+    p = 2;
+  } else {
+    nk = t - su.split - (i - 2 * su.split);
+    k = 0;
+    p = 1;
+  }
+}
+
 constexpr int kClasses = 13;       // tile counts up to kMaxLevels = 4096 -> classes 0..12
 constexpr int kShortTiles = 16;    // users with more tiles are emitted by a whole wave
 
 // LDS scratch of the ordering pass for a workgroup of kThreads.
 template <int kThreads>
 struct OrderScratch {
-  int tot[kClasses];                  // tiles per class
+  int tot[kClasses];                  // tiles (units) per class
   int base[kClasses];                 // next free slot of each class
   int wsum[kThreads / 64][kClasses];  // per-wave class sums of the current chunk
   int long_u[kThreads];               // long users of the current chunk ...
   int long_off[kThreads];             // ... and their first slots
   int nlong;
-  int count;                          // items in the list
+  int count;                          // items (units) in the list
+  int n_whole, n_split;               // list sizes without and with key-range splitting
 };
 
 // Worklist order: users grouped by length class floor(log2(tiles)), highest
@@ -129,24 +165,57 @@ struct OrderScratch {
 // sums in chunks of kThreads users).  emit(slot, user, q_tile, segment) stores
 // one item; S.count receives the number of items.  All threads of the
 // workgroup must call this (it contains barriers).
+//
+// Key-range splitting (sp.p > 1, batches of at most kThreads users only): the
+// same rule and decision as the single-kernel plan (split when the list with
+// split items holds at most sp.upr units), so both plans give the same bits.
+// The counts are then carried packed (whole items in the low 15 bits, units in
+// the high 17) and emit(slot, x, y, segment) gets y = q_tile | kind << 16 and x
+// = the user (kind 0, a whole item) or the split rank of the item's first part
+// (kind 1, 2: first / second part; kind 3: a first part that runs nothing).
+// Without splitting, x = user and y = q_tile.
 template <int kThreads, typename CachePtr, typename Emit>
 __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool cached, int nusers, int total,
-                            int max_tiles, LDS OrderScratch<kThreads>* S, Emit emit) {
+                            int max_tiles, const SplitArgs& sp, LDS OrderScratch<kThreads>* S, Emit emit) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   if (tid < kClasses) S->tot[tid] = 0;
+  if (tid == 0) {
+    S->n_whole = 0;
+    S->n_split = 0;
+  }
   __syncthreads();
+  bool split = false;
+  if (sp.p > 1 && nusers <= kThreads) {  // uniform
+    const int t = tid < nusers ? segment_of(cu, s_cu, cached, tid, total, max_tiles).tiles : 0;
+    int w = t, x = t + split_user(t, 1, sp.min_width).split;
+    for (int o = 32; o > 0; o >>= 1) {
+      w += __shfl_xor(w, o);
+      x += __shfl_xor(x, o);
+    }
+    if (lane == 0) {
+      __atomic_fetch_add(&S->n_whole, w, __ATOMIC_RELAXED);
+      __atomic_fetch_add(&S->n_split, x, __ATOMIC_RELAXED);
+    }
+    __syncthreads();
+    split = S->n_split > S->n_whole && S->n_split <= sp.upr;
+  }
+  // The count a user adds to the list: its q-tiles, or both counts packed.
+  auto units_of_user = [&](int t) {
+    return split ? t | ((t + split_user(t, 1, sp.min_width).split) << 15) : t;
+  };
   // Pass 1: tiles per class (one LDS atomic per class present in a wave).
   for (int u0 = 0; u0 < nusers; u0 += kThreads) {
     const int u = u0 + tid;
     const int t = u < nusers ? segment_of(cu, s_cu, cached, u, total, max_tiles).tiles : 0;
     const int cl = t > 0 ? length_class(t) : -1;
+    const int val = units_of_user(t);
     unsigned long long pending = __ballot(t > 0);
     while (pending) {
       const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
       const bool mine = cl == lc;
-      const int sum = __builtin_amdgcn_readlane(wave_inclusive_sum(mine ? t : 0), 63);
+      const int sum = __builtin_amdgcn_readlane(wave_inclusive_sum(mine ? val : 0), 63);
       if (lane == 0) __atomic_fetch_add(&S->tot[lc], sum, __ATOMIC_RELAXED);
       pending &= ~__ballot(mine);
     }
@@ -156,7 +225,7 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
     const int v = lane < kClasses ? S->tot[kClasses - 1 - lane] : 0;
     const int incl = wave_inclusive_sum(v);
     if (lane < kClasses) S->base[kClasses - 1 - lane] = incl - v;
-    if (lane == kClasses - 1) S->count = incl;
+    if (lane == kClasses - 1) S->count = split ? incl >> 15 : incl;
   }
   // Pass 2: slots, chunk by chunk in ascending user order.
   for (int c0 = 0; c0 < nusers; c0 += kThreads) {
@@ -167,21 +236,43 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
     if (u < nusers) s = segment_of(cu, s_cu, cached, u, total, max_tiles);
     const int t = s.tiles;
     const int cl = t > 0 ? length_class(t) : -1;
-    // Exclusive prefix of the tile counts of earlier lanes in the same class, one
-    // wave scan per class present in the wave.
+    const int val = units_of_user(t);
+    // Exclusive prefix of the counts of earlier lanes in the same class, one wave
+    // scan per class present in the wave.
     int pre = 0;
     unsigned long long pending = __ballot(t > 0);
     while (pending) {
       const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
       const bool mine = cl == lc;
-      const int x = mine ? t : 0;
+      const int x = mine ? val : 0;
       const int incl = wave_inclusive_sum(x);
       if (mine) pre = incl - x;
       if (lane == 63) S->wsum[wid][lc] = incl;
       pending &= ~__ballot(mine);
     }
     __syncthreads();
-    if (t > 0) {
+    if (t > 0 && split) {  // at most kThreads users: a single chunk
+      int both = S->base[cl] + pre;
+      for (int w = 0; w < wid; ++w) both += S->wsum[w][cl];
+      const int off = both >> 15;
+      const int roff = 2 * ((both >> 15) - (both & 0x7fff));
+      const SplitUser spl = split_user(t, 1, sp.min_width);
+      for (int i = 0; i < t + spl.split; ++i) {
+        int nk, k, p;
+        unit_of(t, spl, i, nk, k, p);
+        int kind = 0, x = u;
+        if (p > 1) {
+          const int r0 = roff + i - k;  // split ranks r0, r0+1
+          if (r0 + 2 <= sp.cap) {
+            kind = 1 + k;
+            x = r0;
+          } else if (k == 0) {
+            kind = 3;  // pool full: the second part runs the whole item, the first nothing
+          }
+        }
+        emit(off + i, x, (nk - 1) | (kind << 16), s);
+      }
+    } else if (t > 0) {
       int off = S->base[cl] + pre;
       for (int w = 0; w < wid; ++w) off += S->wsum[w][cl];
       if (t <= kShortTiles) {
@@ -210,11 +301,12 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
   __syncthreads();  // S->count and every emitted item are visible to all threads
 }
 
-// The worklist in global memory: items[slot] = (user, q_tile, row_start, length).
+// The worklist in global memory: items[slot] = (user, q_tile, row_start, length),
+// or with key-range splitting the units described at order_items.
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ cu, int U,
                                                                  int max_tiles, int4* __restrict__ items,
                                                                  int32_t* __restrict__ count,
-                                                                 int32_t* __restrict__ queue) {
+                                                                 int32_t* __restrict__ queue, SplitArgs sp) {
   // The attention kernel's work counters start at zero.
   if (queue != nullptr && threadIdx.x < kQueues) queue[threadIdx.x * kQueueStride] = 0;
   __shared__ int s_cu_lds[kSchedCache + 1];
@@ -228,9 +320,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
   __syncthreads();
   const int total = (U > 0 && max_tiles > 0) ? (cached ? s_cu[U] : cu[U]) : 0;
   const int nusers = max_tiles > 0 ? U : 0;
-  order_items<kSchedThreads>(cu, s_cu, cached, nusers, total, max_tiles, S,
-                             [&](int slot, int u, int k, const Seg& sg) {
-                               items[slot] = make_int4(u, k, sg.start, sg.len);
+  order_items<kSchedThreads>(cu, s_cu, cached, nusers, total, max_tiles, sp, S,
+                             [&](int slot, int x, int y, const Seg& sg) {
+                               items[slot] = make_int4(x, y, sg.start, sg.len);
                              });
   if (threadIdx.x == 0) *count = S->count;
 }
@@ -451,7 +543,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // whole items (kFusedRounds rounds); key-range splitting (below) turns an item
 // into at most kMaxSplitParts work units, so the descriptors hold that many more.
 constexpr int kFusedRounds = 16;
-constexpr int kFusedUsers = kAttnThreads;
+static_assert(kFusedUsers == kAttnThreads, "the shared-list prologue takes one user per thread");
 constexpr int kDescRounds = kFusedRounds * kMaxSplitParts;
 
 // ------------------------------------------------------ key-range splitting
@@ -462,41 +554,6 @@ constexpr int kDescRounds = kFusedRounds * kMaxSplitParts;
 // union of key sets is the rescaled sum of the states over the parts, so the
 // last part to finish folds the others' states into its own and writes the row.
 //
-// Split width of a user of t q-tiles: c = max(ceil(t / 2), min_width) key tiles
-// (0 = no splitting).  Its items with nk > c key tiles (the last t - c q-tiles)
-// run as two parts, key tiles [0, nk/2) and [nk/2, nk) (the diagonal tile in the
-// second); the rest run whole.  The rule depends on the user's own length only.
-// The user's run of work units: the two parts of each split item, q-tiles
-// descending, then its whole items, q-tiles descending.
-struct SplitUser {
-  int c;      // split width (0: no splitting)
-  int split;  // split items: max(t - c, 0)
-};
-
-__device__ __forceinline__ SplitUser split_user(int t, int on, int min_width) {
-  SplitUser r{0, 0};
-  if (on && t > 0) {
-    const int half = (t + 1) >> 1;
-    r.c = half > min_width ? half : min_width;
-    r.split = t > r.c ? t - r.c : 0;
-  }
-  return r;
-}
-
-// Unit i of the run of a user of t q-tiles: its item has nk key tiles and it is
-// part k of p (p = 1: the whole item).
-__device__ __forceinline__ void unit_of(int t, const SplitUser& su, int i, int& nk, int& k, int& p) {
-  if (i < 2 * su.split) {
-    nk = t - (i >> 1);
-    k = i & 1;
-    p = 2;
-  } else {
-    nk = t - su.split - (i - 2 * su.split);
-    k = 0;
-    p = 1;
-  }
-}
-
 // Each part's state goes to a pool slot in global memory, [wave][d][half][lane]
 // float2 for O (4096 floats) then (m, l) per thread (512 floats).  The parts of
 // one item run on different workgroups and possibly different XCDs, whose L2
@@ -586,7 +643,7 @@ __device__ __forceinline__ void merge_parts(const float* slot0, int64_t slot_str
 // units in the same order from cu_seqlens (only for batches with at most
 // kFusedUsers users and kFusedRounds rounds of whole items) and keeps their
 // descriptors; with sp.p > 1 the long items run as key-range parts.
-template <bool kFused>
+template <bool kFused, bool kSplit>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                                  const int4* __restrict__ items,
                                                                  const int32_t* __restrict__ count,
@@ -626,7 +683,6 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   const int G = gridDim.x;
   const bool by_head = G % n_heads == 0;
   const int slots = by_head ? G / n_heads : G;
-  const int units_per_round = G / n_heads;  // (unit, head) pairs of one round / n_heads
   const int slot = by_head ? blockIdx.x / n_heads : blockIdx.x;
   const int head0 = by_head ? blockIdx.x - slot * n_heads : 0;
   auto work_of = [&](int round, int& item, int& h) {
@@ -722,7 +778,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     const int n_whole = n_both & 0x7fff, n_split = n_both >> 15;
     // Split only when every unit of the split list gets a workgroup of its own:
     // then all parts start at once and none waits for a second round.
-    const bool split = n_split > n_whole && n_split <= units_per_round;
+    const bool split = n_split > n_whole && n_split <= sp.upr;
     const int n = split ? n_split : n_whole;
     if (!split) spl = SplitUser{0, 0};
     const int su = t + spl.split;  // work units of this user
@@ -784,7 +840,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     desc_base = one_wave ? L.wid * kDescRounds : 0;
   } else {
     nitems = *count;
-    qt_max = nitems > 0 ? items[0].y : 0;  // the first item is a longest user's last q-tile
+    qt_max = nitems > 0 ? items[0].y & 0xffff : 0;  // the first unit is of a longest user's last q-tile
   }
   // Dynamic assignment (worklist path with work counters): instead of the fixed
   // snake, a workgroup takes the next unclaimed item from a counter in global
@@ -849,10 +905,30 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
         if (item >= nitems) break;
       }
       const int4 it = items[item];
-      qt = it.y;
+      qt = it.y & 0xffff;
       start = it.z;
       len = it.w;
       khi = qt + 1;
+      if constexpr (kSplit) {
+        const int kind = it.y >> 16;  // 0 in a list without split items
+        if (kind == 3) {  // its item runs whole as the second part
+          if (dyn) {      // pass the claim on once every wave has read s_next
+            lds_barrier();
+            if (threadIdx.x == 0) s_next = claimed;
+            lds_barrier();
+          }
+          continue;
+        }
+        if (kind != 0) {  // key tiles [0, nk/2) or [nk/2, nk)
+          parts = 2;
+          part = kind - 1;
+          rank0 = it.x;
+          if (part == 0)
+            khi >>= 1;
+          else
+            klo = khi >> 1;
+        }
+      }
     }
     const int q0 = qt * kTileRows;
     const int lim = len - 1 - q0;  // the user's last row, relative to the diagonal tile
@@ -928,7 +1004,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     // Tile j of the range sits in stage (j - klo) % 2.  Only the diagonal tile
     // (qt, the last tile of the range when khi == qt + 1) needs a mask; the last
     // tile of a first part goes through the same masked step with nothing masked.
-    const int mlim = (!kFused || khi == qt + 1) ? L.qr : kTileRows - 1;
+    const int mlim = (!kSplit || khi == qt + 1) ? L.qr : kTileRows - 1;
     int j = klo;
     for (; j + 2 < khi; j += 2) {
       wait_and_barrier<0>();
@@ -953,7 +1029,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
     if (dyn && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring before the next item refills it
 
-    if (parts > 1) {
+    if (kSplit && parts > 1) {
       // Leave this part's state in its slot; count the arrival once every wave's
       // stores have completed.  The last part to arrive resets the counter for
       // the next call and merges; the others are done with this unit.
@@ -990,24 +1066,29 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
 }  // namespace
 
 hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles, int4* items, int32_t* count,
-                           int32_t* queue, hipStream_t stream) {
+                           int32_t* queue, const SplitArgs& split, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens, num_users, max_tiles,
-                     items, count, queue);
+                     items, count, queue, split);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue, int n_heads,
-                            float scale_log2e, void* out, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attention_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, scale_log2e,
-                     SplitArgs{0, 0, 0, nullptr, nullptr}, static_cast<uint16_t*>(out));
+                            float scale_log2e, const SplitArgs& split, void* out, int grid, hipStream_t stream) {
+  if (split.p > 1)
+    hipLaunchKernelGGL((attention_kernel<false, true>), dim3(grid), dim3(kAttnThreads), 0, stream,
+                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, scale_log2e,
+                       split, static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL((attention_kernel<false, false>), dim3(grid), dim3(kAttnThreads), 0, stream,
+                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, scale_log2e,
+                       split, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
                                   int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
                                   hipStream_t stream) {
-  hipLaunchKernelGGL(attention_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((attention_kernel<true, true>), dim3(grid), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(qkv), nullptr, nullptr, nullptr, cu_seqlens, num_users, max_tiles,
                      n_heads, scale_log2e, split, static_cast<uint16_t*>(out));
   return hipGetLastError();
@@ -1023,8 +1104,9 @@ bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t g
 
 int attention_blocks_per_cu(bool fused) {
   int n = 0;
-  const hipError_t e = fused ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<true>, kAttnThreads, 0)
-                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<false>, kAttnThreads, 0);
+  const hipError_t e =
+      fused ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<true, true>, kAttnThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<false, false>, kAttnThreads, 0);
   if (e != hipSuccess || n < 1) n = 1;
   return n;
 }
