@@ -19,6 +19,9 @@
 //    user.  After the scheduler kernel, workgroups claim items from one counter
 //    per head; in the single-kernel plan (and over a caller's worklist) each
 //    workgroup takes a fixed snake over the list.
+//  * Key-range splitting -- in small batches whose units all fit one round of
+//    the grid, the longest items run as two parts over disjoint key ranges on
+//    two workgroups; the last part to finish merges the two (m, l, acc) states.
 //
 // Attention workgroup: 4 waves; wave w owns query rows 16w..16w+15 of the tile.
 //  * K and V tiles (64 keys x 64 dims, 8 KB each) are copied from HBM straight
