@@ -227,8 +227,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(users shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(users would shard across GPUs with no exchange between them).", file=sys.stderr)
         sys.exit(2)
 
     import torch
