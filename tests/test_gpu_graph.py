@@ -14,11 +14,25 @@ from gpu_util import say, to_gpu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3])
-def test_graph_replay_matches_eager(gpu, idx):
-    w = workloads.make_config(idx)
+SPLIT_LENGTHS = [1000, 700, 3, 450, 0, 320]
+
+GRAPH_CASES = [
+    ("config 1", lambda: workloads.make_config(1)),
+    ("config 2", lambda: workloads.make_config(2)),
+    ("config 3", lambda: workloads.make_config(3)),
+    # Long items split into key-range parts (the pool exists after the eager call),
+    # on the single-kernel plan and, with a larger max_seqlen, on the scheduler plan.
+    ("split items, single kernel", lambda: workloads.make_from_lengths(SPLIT_LENGTHS, seed=13)),
+    ("split items, scheduler plan", lambda: workloads.make_from_lengths(SPLIT_LENGTHS, seed=13, max_seqlen=65536)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GRAPH_CASES)))
+def test_graph_replay_matches_eager(gpu, case):
+    name, make = GRAPH_CASES[case]
+    w = make()
     single = vlca.single_kernel(w.num_users, w.max_seqlen, w.n_heads)
-    say(f"[case] graph capture of fwd, config {idx} ({w.name}), single kernel: {single}")
+    say(f"[case] graph capture of fwd, {name} ({w.name}), single kernel: {single}")
     qkv, cu = to_gpu(w)
     s = torch.cuda.Stream()
     out = torch.zeros((w.total_tokens, 512), dtype=torch.bfloat16, device="cuda")
@@ -80,7 +94,7 @@ def test_concurrent_streams_single_kernel_split(gpu):
     parts: each stream has its own pool of part states and arrival counters, and
     every call leaves the counters ready for the next."""
     wa = workloads.make_config(2)
-    wb = workloads.make_from_lengths([1000, 700, 3, 450, 0, 320], seed=13)
+    wb = workloads.make_from_lengths(SPLIT_LENGTHS, seed=13)
     for w in (wa, wb):
         assert vlca.single_kernel(w.num_users, w.max_seqlen, w.n_heads)
     say(f"[case] concurrent split single-kernel fwd on two streams: {wa.name} and lengths {list(wb.lengths)}")
