@@ -82,6 +82,22 @@ def sample_rows(w, rng, per_long=160, max_short_rows=2500):
     return np.unique(np.asarray(rows, dtype=np.int64))
 
 
+# Equal users whose items all fit in one round of a full grid: the single-kernel
+# plan deals them with the snake across each CU's workgroups (on a 256-CU device).
+BALANCED_CASES = {"4x2048": [2048] * 4, "8x1024": [1024] * 8, "2x4096": [4096] * 2}
+
+
+@pytest.mark.parametrize("name", sorted(BALANCED_CASES))
+def test_balanced_one_round_sampled_rows(gpu, name):
+    w = workloads.make_from_lengths(BALANCED_CASES[name], seed=21)
+    say(f"[case] balanced batch {name} T={w.total_tokens}")
+    out = run_fwd(w)
+    assert np.all(np.isfinite(out.float().numpy()))
+    rows = sample_rows(w, np.random.default_rng(21))
+    ref = oracle.varlen_causal_attention_rows(qkv64(w), w.cu_seqlens, rows, w.n_heads, w.head_dim, w.scale)
+    assert_close(out[rows], ref, f"{name} ({rows.size} sampled rows)")
+
+
 @pytest.mark.parametrize("idx", [4, 5])
 def test_configs_sampled_rows(gpu, idx):
     w = workloads.make_config(idx)

@@ -45,6 +45,7 @@ std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 std::map<std::pair<int, hipStream_t>, SplitPool> g_pools;
 std::map<int, int> g_resident;  // 2*device + fused -> resident attention workgroups
+std::map<int, int> g_cus;       // device -> compute units
 
 int64_t max_tiles_of(int max_seqlen) { return (static_cast<int64_t>(max_seqlen) + vlca::kTileRows - 1) / vlca::kTileRows; }
 
@@ -72,15 +73,25 @@ int check_attention_args(const void* qkv, const int32_t* cu_seqlens, int num_use
   return VLCA_OK;
 }
 
+// Compute units of a device.
+int cu_count(int dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_cus[dev] = n;
+  return n;
+}
+
 // Resident attention workgroups per device: CUs x workgroups per CU, for the
 // kernel over a worklist or the single-kernel variant.
 int resident_blocks(int dev, bool fused) {
+  const int n = cu_count(dev);
   std::lock_guard<std::mutex> lk(g_mu);
   const int key = 2 * dev + (fused ? 1 : 0);
   auto it = g_resident.find(key);
   if (it != g_resident.end()) return it->second;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
   const int r = n * vlca::attention_blocks_per_cu(fused);
   g_resident[key] = r;
   return r;
@@ -95,6 +106,22 @@ int grid_size(int dev, int64_t work, bool fused) {
   if (g < 8) g = 8;
   if (work < g) g = work;
   return static_cast<int>(g);
+}
+
+// The kernel's `layer_log2` argument.  With every unit in one round of the
+// fixed assignment (at most max_units units per head), log2 of the slots between
+// workgroups that share a CU (workgroups g and g + CUs in launch order; a
+// workgroup's slot is g / H with the grid a multiple of H, else g), when that is
+// a power of two smaller than the slots; -1 otherwise (plain snake).
+int snake_layer_log2(int dev, int grid, int n_heads, int64_t max_units) {
+  const bool by_head = grid % n_heads == 0;
+  const int64_t slots = by_head ? grid / n_heads : grid;
+  if ((by_head ? max_units : max_units * n_heads) > slots) return -1;
+  const int cus = cu_count(dev);
+  if (by_head && cus % n_heads != 0) return -1;
+  const int layer = by_head ? cus / n_heads : cus;
+  if (layer < 1 || (layer & (layer - 1)) != 0 || layer >= slots) return -1;
+  return __builtin_ctz(static_cast<unsigned>(layer));
 }
 
 int64_t item_pairs(int num_users, int max_seqlen, int n_heads) {
@@ -179,8 +206,10 @@ int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int m
   int64_t pairs = item_pairs(num_users, max_seqlen, n_heads);
   if (split.p > 1) pairs *= kSplitParts;
   const int grid = grid_size(dev, pairs, false);
-  if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, split, out, grid, stream) !=
-      hipSuccess)
+  const int layer_log2 =
+      queue ? -1 : snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
+  if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, split, out, grid, layer_log2,
+                             stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
@@ -219,8 +248,9 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   }
   if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
     if (split.p > 1) grid = grid_size(dev, pairs * kSplitParts, true);
+    const int layer_log2 = snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
     if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, split, out,
-                                     grid, stream) != hipSuccess)
+                                     grid, layer_log2, stream) != hipSuccess)
       return VLCA_ERR_HIP;
     return VLCA_OK;
   }

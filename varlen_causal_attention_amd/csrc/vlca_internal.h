@@ -44,16 +44,20 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 
 // Attention: persistent grid walking the first *count items.  queue null: a fixed
 // assignment of items to workgroups; otherwise workgroups claim items from the
-// zeroed counters at queue (reset by launch_schedule).
+// zeroed counters at queue (reset by launch_schedule).  layer_log2: -1, or (when
+// the work is known to fit in one round of the fixed assignment) log2 of the
+// slots between workgroups that share a CU, so that the assignment balances each
+// CU's items.
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue, int n_heads,
-                            float scale_log2e, const SplitArgs& split, void* out, int grid, hipStream_t stream);
+                            float scale_log2e, const SplitArgs& split, void* out, int grid, int layer_log2,
+                            hipStream_t stream);
 
 // Attention alone with the ordering done inside the kernel (no worklist buffer):
 // for batches where fused_fits() holds.  split.p == 2 splits long items (needs
 // split.pool / split.ctr).
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
                                   int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
-                                  hipStream_t stream);
+                                  int layer_log2, hipStream_t stream);
 bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid);
 
 // Users the single-kernel plan takes at most (one per lane of four chunks).

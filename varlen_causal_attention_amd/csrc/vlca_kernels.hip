@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
                                                                  const int32_t* __restrict__ count,
                                                                  int32_t* __restrict__ queue,
                                                                  const int32_t* __restrict__ cu, int U, int max_tiles,
-                                                                 int n_heads, float sl2, SplitArgs sp,
+                                                                 int n_heads, int layer_log2, float sl2, SplitArgs sp,
                                                                  uint16_t* __restrict__ out) {
   // Two ring stages (K tile then V tile); tile j of an item lives in stage j%2.
   // The key loop is unrolled by two so that every LDS address is a per-lane
@@ -688,8 +688,25 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
   const int slots = by_head ? G / n_heads : G;
   const int slot = by_head ? blockIdx.x / n_heads : blockIdx.x;
   const int head0 = by_head ? blockIdx.x - slot * n_heads : 0;
+  // When all the work fits in one round, the workgroups that share a CU
+  // (g, g + CUs, g + 2 CUs, ... in launch order) hold slots `layer` apart, and
+  // the snake runs across them instead: odd layers take their ranks in reverse,
+  // so the sums of the items on each CU come out even rather than the first CUs
+  // drawing the longest item of every layer.  With more rounds the plain snake
+  // is kept: it leaves the second round's items to the CUs of the shortest
+  // first-round items, away from the longest ones.
+  // (Every round after the first is then empty, so the layered rank can stand
+  // in for the slot in every round.)  The launch passes layer_log2 >= 0 only
+  // when the work fits in one round and `layer` is a power of two.
+  int rank = slot;
+  if (layer_log2 >= 0) {
+    const int layer = 1 << layer_log2;
+    const int lyr = slot >> layer_log2, lyr_pos = slot & (layer - 1);
+    const int lyr_len = min(layer, slots - (lyr << layer_log2));
+    rank = slot - lyr_pos + ((lyr & 1) ? lyr_len - 1 - lyr_pos : lyr_pos);
+  }
   auto work_of = [&](int round, int& item, int& h) {
-    const int pos = (round & 1) ? slots - 1 - slot : slot;
+    const int pos = (round & 1) ? slots - 1 - rank : rank;
     if (by_head) {
       item = round * slots + pos;
       h = head0;
@@ -1076,24 +1093,25 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 }
 
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue, int n_heads,
-                            float scale_log2e, const SplitArgs& split, void* out, int grid, hipStream_t stream) {
+                            float scale_log2e, const SplitArgs& split, void* out, int grid, int layer_log2,
+                            hipStream_t stream) {
   if (split.p > 1)
     hipLaunchKernelGGL((attention_kernel<false, true>), dim3(grid), dim3(kAttnThreads), 0, stream,
-                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, scale_log2e,
-                       split, static_cast<uint16_t*>(out));
+                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, layer_log2,
+                       scale_log2e, split, static_cast<uint16_t*>(out));
   else
     hipLaunchKernelGGL((attention_kernel<false, false>), dim3(grid), dim3(kAttnThreads), 0, stream,
-                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, scale_log2e,
-                       split, static_cast<uint16_t*>(out));
+                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, layer_log2,
+                       scale_log2e, split, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
                                   int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
-                                  hipStream_t stream) {
+                                  int layer_log2, hipStream_t stream) {
   hipLaunchKernelGGL((attention_kernel<true, true>), dim3(grid), dim3(kAttnThreads), 0, stream,
                      static_cast<const uint16_t*>(qkv), nullptr, nullptr, nullptr, cu_seqlens, num_users, max_tiles,
-                     n_heads, scale_log2e, split, static_cast<uint16_t*>(out));
+                     n_heads, layer_log2, scale_log2e, split, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
