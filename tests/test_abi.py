@@ -122,3 +122,37 @@ def test_single_kernel_query_validation():
     assert f(4, 40, 0, ctypes.byref(flag)) == -4
     assert f(4, 40, 8, None) == -1
     assert flag.value == 7
+
+
+def _tramp_args(qkv=FAKE, cu=FAKE, U=4, ms=40, H=8, D=64, scale=0.125, out=FAKE * 2):
+    return (0 if qkv is None else qkv, 0 if cu is None else cu, U, ms, H, D, scale, 0 if out is None else out, 0)
+
+
+def test_call_module_is_built_and_bound():
+    assert vlca.call_module() is not None, "the CPython call module was not built"
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(U=-1), dict(D=128), dict(H=0), dict(scale=float("nan")), dict(scale=0.0), dict(ms=262145),
+    dict(qkv=None), dict(out=None), dict(out=FAKE), dict(U=0, qkv=None, cu=None, out=None), dict(ms=0),
+])
+def test_call_module_passes_arguments_like_ctypes(kwargs):
+    # Both routes reach the same validation (no device work): equal return codes.
+    m = vlca.call_module()
+    a = _tramp_args(**kwargs)
+    assert m.fwd(*a) == _fwd(**kwargs)
+    w = a[:7] + (FAKE, 5000, FAKE) + a[7:]  # items, capacity, count before out, stream
+    ref = vlca.library().varlen_causal_attn_fwd_worklist(*w[:6], ctypes.c_float(w[6]), *w[7:])
+    assert m.fwd_worklist(*w) == ref
+
+
+def test_call_module_rejects_bad_python_arguments():
+    m = vlca.call_module()
+    with pytest.raises(TypeError):
+        m.fwd(*_tramp_args()[:8])
+    with pytest.raises(TypeError):
+        m.fwd(*_tramp_args(U="4"))
+    with pytest.raises(OverflowError):
+        m.fwd(*_tramp_args(U=2**40))
+    with pytest.raises(TypeError):
+        m.fwd_worklist(*_tramp_args())

@@ -14,12 +14,13 @@ from typing import Optional, Tuple
 
 __all__ = [
     "VlcaError", "library", "library_path", "fwd", "build_worklist", "fwd_with_worklist",
-    "worklist_capacity", "single_kernel", "tile_rows", "strerror", "EXPORTED_SYMBOLS",
+    "worklist_capacity", "single_kernel", "tile_rows", "strerror", "call_module", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libvlca.so")
 _lib = None
+_call = None  # the CPython trampoline for fwd / fwd_worklist (ctypes when it is not built)
 
 EXPORTED_SYMBOLS = (
     "varlen_causal_attn_fwd",
@@ -67,8 +68,23 @@ def library():
     lib.varlen_causal_attn_tile_rows.restype = c_int
     lib.varlen_causal_attn_strerror.argtypes = [c_int]
     lib.varlen_causal_attn_strerror.restype = ctypes.c_char_p
+    global _call
+    try:
+        from . import _vlca_call
+    except ImportError:
+        _vlca_call = None
+    if _vlca_call is not None:
+        _vlca_call.set_entries(ctypes.cast(lib.varlen_causal_attn_fwd, vp).value,
+                               ctypes.cast(lib.varlen_causal_attn_fwd_worklist, vp).value)
+        _call = _vlca_call
     _lib = lib
     return lib
+
+
+def call_module():
+    """The CPython call trampoline in use for fwd / fwd_worklist, or None (ctypes)."""
+    library()
+    return _call
 
 
 def strerror(code: int) -> str:
@@ -161,9 +177,10 @@ def fwd(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
     out = _out_tensor(qkv, n_heads, head_dim, out)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
-    rc = library().varlen_causal_attn_fwd(qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1, int(max_seqlen),
-                                          int(n_heads), int(head_dim), float(scale), out.data_ptr(),
-                                          _stream_handle(qkv.device))
+    lib = library()
+    args = (qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1, int(max_seqlen), int(n_heads), int(head_dim),
+            float(scale), out.data_ptr(), _stream_handle(qkv.device))
+    rc = _call.fwd(*args) if _call is not None else lib.varlen_causal_attn_fwd(*args)
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd")
     return out
@@ -201,10 +218,11 @@ def fwd_with_worklist(qkv, cu_seqlens, max_seqlen: int, items, count, n_heads: i
     out = _out_tensor(qkv, n_heads, head_dim, out)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
-    rc = library().varlen_causal_attn_fwd_worklist(qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1,
-                                                   int(max_seqlen), int(n_heads), int(head_dim), float(scale),
-                                                   items.data_ptr(), items.shape[0], count.data_ptr(),
-                                                   out.data_ptr(), _stream_handle(qkv.device))
+    lib = library()
+    args = (qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1, int(max_seqlen), int(n_heads), int(head_dim),
+            float(scale), items.data_ptr(), items.shape[0], count.data_ptr(), out.data_ptr(),
+            _stream_handle(qkv.device))
+    rc = _call.fwd_worklist(*args) if _call is not None else lib.varlen_causal_attn_fwd_worklist(*args)
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd_worklist")
     return out

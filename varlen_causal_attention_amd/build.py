@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+import sysconfig
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -16,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvlca.so")
 SOURCES = [os.path.join(CSRC, "vlca_kernels.hip"), os.path.join(CSRC, "vlca_api.cpp")]
+# The CPython call trampoline (argument marshalling for the two launch entry points).
+CALL_SOURCE = os.path.join(CSRC, "vlca_pyext.c")
+CALL_MODULE = os.path.join(PKG, "_vlca_call" + (sysconfig.get_config_var("EXT_SUFFIX") or ".so"))
 
 # Packed fp32 VALU forms are disabled for all device code.  MFMA results are kept
 # in VGPRs (not AGPRs): the softmax reads every score and rescales the
@@ -48,7 +52,25 @@ def build(verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
     os.replace(tmp, LIB)
+    build_call_module(verbose)
     return LIB
+
+
+def build_call_module(verbose: bool = False) -> str:
+    """Compile the CPython trampoline (host C only, no HIP)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the call module")
+    tmp = CALL_MODULE + ".tmp"
+    cmd = [cc, "-O2", "-shared", "-fPIC", "-Wall", "-I", sysconfig.get_paths()["include"], "-I", INCLUDE,
+           CALL_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the call module failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, CALL_MODULE)
+    return CALL_MODULE
 
 
 if __name__ == "__main__":
