@@ -18,8 +18,7 @@
 //    one head's K/V columns and serves the re-reads of later q-tiles of the same
 //    user.  After the scheduler kernel, workgroups claim items from one counter
 //    per head; in the single-kernel plan (and over a caller's worklist) each
-//    workgroup takes a fixed snake over the list, dealt across the workgroups
-//    that share a CU when all the work fits one round.
+//    workgroup takes a fixed snake over the list.
 //  * Key-range splitting -- in small batches whose units all fit one round of
 //    the grid, the longest items run as two parts over disjoint key ranges on
 //    two workgroups; the last part to finish merges the two (m, l, acc) states.
