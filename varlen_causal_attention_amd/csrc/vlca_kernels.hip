@@ -18,7 +18,8 @@
 //    one head's K/V columns and serves the re-reads of later q-tiles of the same
 //    user.  After the scheduler kernel, workgroups claim items from one counter
 //    per head; in the single-kernel plan (and over a caller's worklist) each
-//    workgroup takes a fixed snake over the list.
+//    workgroup takes a fixed snake over the list, dealt across the workgroups
+//    that share a CU when all the work fits one round.
 //  * Key-range splitting -- in small batches whose units all fit one round of
 //    the grid, the longest items run as two parts over disjoint key ranges on
 //    two workgroups; the last part to finish merges the two (m, l, acc) states.
@@ -58,6 +59,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS __attribute__((address_space(3)))
 typedef LDS bf16x4 lds_bf16x4;
@@ -647,13 +649,10 @@ __device__ __forceinline__ void merge_parts(const float* slot0, int64_t slot_str
 // kFusedUsers users and kFusedRounds rounds of whole items) and keeps their
 // descriptors; with sp.p > 1 the long items run as key-range parts.
 template <bool kFused, bool kSplit>
-__global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t* __restrict__ qkv,
-                                                                 const int4* __restrict__ items,
-                                                                 const int32_t* __restrict__ count,
-                                                                 int32_t* __restrict__ queue,
-                                                                 const int32_t* __restrict__ cu, int U, int max_tiles,
-                                                                 int n_heads, int layer_log2, float sl2, SplitArgs sp,
-                                                                 uint16_t* __restrict__ out) {
+__device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv, const int4* __restrict__ items,
+                                               const int32_t* __restrict__ count, int32_t* __restrict__ queue,
+                                               const int32_t* __restrict__ cu, int U, int max_tiles, int n_heads,
+                                               int layer_log2, float sl2, SplitArgs sp, uint16_t* __restrict__ out) {
   // Two ring stages (K tile then V tile); tile j of an item lives in stage j%2.
   // The key loop is unrolled by two so that every LDS address is a per-lane
   // register plus an immediate.
@@ -1069,19 +1068,60 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const uint16_t*
       merge_parts(slot0, slot_stride, parts, part, L, sl2, A);
     }
 
-    if (L.qr < len - q0) {
+    {
+      // The wave's 16 output rows go through its own rows of stage 0's K half
+      // (every wave is past the item's last barrier, and only this wave copies into
+      // those rows, after these reads), so that each row leaves as one 128-byte
+      // write of 8 lanes instead of four 32-byte pieces from four instructions.
+      // 16-byte chunk c of row r sits at chunk c ^ (r % 8): conflict-free both ways.
+      // The lane id passes through an empty asm so that the addresses are formed
+      // here rather than kept live across the item loop.
+      int lane = L.lane;
+      asm volatile("" : "+v"(lane));
+      const int lq = lane & 15, g = lane >> 4;
+      LDS char* const rows = st0 + 2048 * L.wid;
       const float inv = 1.0f / A.l[0];
-      uint16_t* o = out + ((int64_t)start + q0 + L.qr) * ldo + h * kHeadDim + 4 * L.g;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint2 wv;
-        wv.x = pack_bf16x2(A.o[d][0] * inv, A.o[d][1] * inv);
-        wv.y = pack_bf16x2(A.o[d][2] * inv, A.o[d][3] * inv);
-        *reinterpret_cast<uint2*>(o + 16 * d) = wv;
+      for (int d = 0; d < 4; ++d) {  // dims 16d + 4g .. +3 of row lq: bytes 32d + 8g
+        const u32x2 wv = {pack_bf16x2(A.o[d][0] * inv, A.o[d][1] * inv),
+                          pack_bf16x2(A.o[d][2] * inv, A.o[d][3] * inv)};
+        *(LDS u32x2*)(rows + lq * 128 + (((2 * d + (g >> 1)) ^ swz(lq)) << 4) + 8 * (g & 1)) = wv;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {  // row r: lanes 8(r%8) .. +7, one 16-byte chunk each
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const u32x4 v = *(const LDS u32x4*)(rows + r * 128 + ((c ^ swz(r)) << 4));
+        if (16 * L.wid + r < len - q0)
+          *reinterpret_cast<u32x4*>(out + ((int64_t)start + q0 + 16 * L.wid + r) * ldo + h * kHeadDim + 8 * c) = v;
       }
     }
   }
 }
+
+#define VLCA_ATTENTION_PARAMS                                                                                   \
+  const uint16_t *__restrict__ qkv, const int4 *__restrict__ items, const int32_t *__restrict__ count,          \
+      int32_t *__restrict__ queue, const int32_t *__restrict__ cu, int U, int max_tiles, int n_heads,             \
+      int layer_log2, float sl2, SplitArgs sp, uint16_t *__restrict__ out
+#define VLCA_ATTENTION_ARGS qkv, items, count, queue, cu, U, max_tiles, n_heads, layer_log2, sl2, sp, out
+
+// Four workgroups per CU (128 VGPRs a lane) is the occupancy the tile step is
+// tuned for.  The split-capable worklist instance needs the occupancy bound to
+// stay there (129 VGPRs without it); on the other instances, which fit anyway,
+// the bound made the compiler schedule the tile step worse (the 25523-token
+// batch 8% slower), so they do without.
+template <bool kFused, bool kSplit>
+__global__ __launch_bounds__(kAttnThreads) void attention_kernel(VLCA_ATTENTION_PARAMS) {
+  attention_body<kFused, kSplit>(VLCA_ATTENTION_ARGS);
+}
+
+template <>
+__global__ __launch_bounds__(kAttnThreads, 4) void attention_kernel<false, true>(VLCA_ATTENTION_PARAMS) {
+  attention_body<false, true>(VLCA_ATTENTION_ARGS);
+}
+
+#undef VLCA_ATTENTION_ARGS
+#undef VLCA_ATTENTION_PARAMS
 
 }  // namespace
 
