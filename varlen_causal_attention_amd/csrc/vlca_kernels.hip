@@ -1092,8 +1092,11 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       for (int i = 0; i < 2; ++i) {  // row r: lanes 8(r%8) .. +7, one 16-byte chunk each
         const int r = 8 * i + (lane >> 3), c = lane & 7;
         const u32x4 v = *(const LDS u32x4*)(rows + r * 128 + ((c ^ swz(r)) << 4));
+        // Non-temporal: the kernel never reads the output back, so its lines need
+        // not displace K/V in L2.
         if (16 * L.wid + r < len - q0)
-          *reinterpret_cast<u32x4*>(out + ((int64_t)start + q0 + 16 * L.wid + r) * ldo + h * kHeadDim + 8 * c) = v;
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<u32x4*>(out + ((int64_t)start + q0 + 16 * L.wid + r) * ldo + h * kHeadDim + 8 * c));
       }
     }
   }
