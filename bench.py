@@ -87,15 +87,15 @@ def cpu_baseline(w, budget_s: float):
 
 
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {r}/gpurun_out/prof/trace -o run -- "
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o run -- "
              "python3 {r}/bench.py --config {c} --steps 200 --warmup 2000 --no-cpu-baseline --cold-steps 0",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {r}/gpurun_out/prof/fetch -o run -- "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/fetch -o run -- "
              "python3 {r}/bench.py --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {r}/gpurun_out/prof/write -o run -- "
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run -- "
              "python3 {r}/bench.py --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
-    "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {r}/gpurun_out/prof/copyf -o run -- "
+    "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/copyf -o run -- "
              "python3 {r}/bench.py --calibrate-copy-mib 256 --steps 5",
-    "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {r}/gpurun_out/prof/copyw -o run -- "
+    "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/copyw -o run -- "
              "python3 {r}/bench.py --calibrate-copy-mib 256 --steps 5",
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -121,7 +121,8 @@ def summarize_profiles(root: str, config: int) -> None:
     """Write profiles/attention_kernel_<workload>_{trace,pmc}.txt from rocprofv3 CSV output.
 
     ``root`` holds one folder per rocprofv3 run (commands in PROFILE_COMMANDS, with
-    $REPO the repository root, run from /tmp with TMPDIR=/tmp), plus
+    $REPO the repository root and $OUT the directory given to the runs, here
+    ``root``; run from /tmp with TMPDIR=/tmp), plus
     ``kernel_sha.txt`` (sha256 of the kernel source the runs used) and, optionally,
     ``trace.log`` (that run's stdout/stderr with the bench line).
     """
@@ -133,7 +134,7 @@ def summarize_profiles(root: str, config: int) -> None:
     if sha != kernel_source_hash():
         print(f"warning: profiles were taken on kernel source {sha}, tree has {kernel_source_hash()}",
               file=sys.stderr)
-    cmds = {k: "cd /tmp && export TMPDIR=/tmp && " + v.format(r="$REPO", c=config)
+    cmds = {k: "cd /tmp && export TMPDIR=/tmp && " + v.format(r="$REPO", out="$OUT", c=config)
             for k, v in PROFILE_COMMANDS.items()}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
 
