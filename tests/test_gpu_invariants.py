@@ -231,3 +231,30 @@ def test_bad_shapes_raise(gpu):
         vlca.fwd(qkv.float(), cu, 40)
     with pytest.raises(vlca.VlcaError):
         vlca.fwd(qkv, cu, 40, scale=-1.0)
+
+
+# Rows past cu_seqlens[-1] belong to no user: fwd must leave them as they were,
+# whatever tile a user's last rows fall into.  The batches end in short users, so
+# their diagonal tiles reach into the padding.
+PADDED_CASES = [
+    ("single kernel", [37, 3, 130, 1, 5], None),
+    ("scheduler plan", [37, 3, 130, 1, 5], 65536),
+    ("split items, single kernel", [700, 2, 450, 9], None),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PADDED_CASES)))
+def test_rows_past_the_last_user_untouched(gpu, case):
+    name, lengths, max_seqlen = PADDED_CASES[case]
+    w = workloads.make_from_lengths(lengths, seed=17)
+    pad = 100
+    say(f"[case] padded buffers ({name}): lengths {lengths}, {pad} rows past the end")
+    qkv = torch.cat([w.qkv_bf16, torch.ones((pad, w.qkv_bf16.shape[1]), dtype=torch.bfloat16)]).cuda()
+    cu = torch.from_numpy(np.asarray(w.cu_seqlens, dtype=np.int32)).cuda()
+    out = torch.full((w.total_tokens + pad, 512), 7.0, dtype=torch.bfloat16, device="cuda")
+    vlca.fwd(qkv, cu, w.max_seqlen if max_seqlen is None else max_seqlen, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert bool((out[w.total_tokens:] == 7.0).all()), "fwd wrote rows past the last user"
+    ref = oracle.varlen_causal_attention(qkv64(w), w.cu_seqlens, w.n_heads, w.head_dim, w.scale)
+    assert_close(out[: w.total_tokens], ref, name)
