@@ -101,17 +101,18 @@ def block_diagonal_causal_mask(cu_seqlens) -> np.ndarray:
     """Dense boolean ``[T, T]`` mask: entry (i, j) is True iff rows i and j belong to
     the same user and j <= i.
 
-    Built the way the plan 2026-06-14-cti-auc-recovery, Task 9, Step 3 builds it:
-    a per-row user id (each user index repeated by its length), equality of ids,
-    and a lower-triangular matrix over the whole stream.
+    This is the mask that the plan 2026-06-14-cti-auc-recovery (Task 9, Step 3)
+    applies to the whole packed stream.  Here it is formed from its definition:
+    users own contiguous row ranges, so "same user and j <= i" holds exactly when
+    the first row of row i's user is <= j <= i.
     """
     cu = np.asarray(cu_seqlens, dtype=np.int64)
-    lengths = np.diff(cu)
-    uid = np.repeat(np.arange(lengths.shape[0]), lengths)
-    same = uid[None, :] == uid[:, None]
-    T = uid.shape[0]
-    lower = np.tril(np.ones((T, T), dtype=bool))
-    return same & lower
+    T = int(cu[-1])
+    rows = np.arange(T)
+    # The user owning row r is the last u with cu[u] <= r (zero-length users own no row).
+    first = cu[np.searchsorted(cu, rows, side="right") - 1]
+    cols = rows[None, :]
+    return (cols >= first[:, None]) & (cols <= rows[:, None])
 
 
 def dense_masked_attention(qkv: np.ndarray, cu_seqlens, n_heads: int, head_dim: int,
