@@ -66,34 +66,43 @@ enum {
   VLCA_ERR_TOO_LARGE = -6,       /* max_seqlen > VLCA_MAX_SEQLEN or worklist > 2^31  */
   VLCA_ERR_CAPACITY = -7,        /* caller worklist buffer smaller than required     */
   VLCA_ERR_ALIAS = -8,           /* qkv and out are the same pointer                 */
-  VLCA_ERR_WORKSPACE = -9,       /* library workspace could not be (re)allocated,
-                                    or would need to grow while the stream captures  */
+  VLCA_ERR_WORKSPACE = -9,       /* library workspace could not be allocated        */
   VLCA_ERR_HIP = -10             /* a HIP runtime call or kernel launch failed       */
 };
 
 /*
  * Forward pass.  Runs the segment scheduler (a compact (user, q-tile) worklist:
- * users grouped by length class floor(log2(q-tiles)), longest class first, each
- * user's q-tiles adjacent, last q-tile first) and the attention kernel on
- * `stream`.
- * Small batches (num_users <= 256 and num_users*ceil(max_seqlen/64)*n_heads at most
- * 16 items per resident workgroup; varlen_causal_attn_single_kernel() tells) run
- * as one kernel in which every workgroup locates its own items.  In a batch of
- * at most 256 users whose items, with the long ones split, fit in one round of
- * resident workgroups, the items of more than max(ceil(t/2), 4) key tiles of a
- * user of t q-tiles run as two key-range parts whose softmax states are merged
- * (on either plan, with the same decision, so max_seqlen does not change the
- * bits).  The parts meet in a fixed-size pool (about 38 MB) kept per (device,
- * stream), allocated by the first call on a stream that may split (hipMalloc;
- * while the stream is being captured and has no pool yet, the call runs its
- * items whole instead).  Split and whole items agree within rounding; the
- * worklist entry points below always run items whole.  Larger batches keep their worklist
- * in a library-owned device buffer kept per (device, stream) and grown on demand:
- * the first call on a stream with a larger num_users*ceil(max_seqlen/64) allocates
- * it (hipMalloc) after synchronising that stream, which is not allowed while the
- * stream is being captured (VLCA_ERR_WORKSPACE then -- make one eager call of the
- * same or larger size first).  Two calls that overlap on the same stream cannot
- * happen (stream order); calls on different streams use different buffers.
+ * users grouped by length class floor(log2(q-tiles)), longest class first, users
+ * ascending inside a class, each user's q-tiles adjacent, last q-tile first) and
+ * the attention kernel on `stream`.
+ *
+ * Launch plans.  Small batches (num_users <= 256 and
+ * num_users*ceil(max_seqlen/64)*n_heads at most 16 items per resident
+ * workgroup; varlen_causal_attn_single_kernel() tells) run as one kernel in
+ * which every workgroup locates its own items.  Larger batches run the
+ * scheduler kernel and the attention kernel over a worklist.
+ *
+ * Key-range splitting.  When the batch's users with rows, with the long items
+ * split, give at most one round of resident workgroups' work units, the items
+ * of more than max(ceil(t/2), 4) key tiles of a user of t q-tiles run as two
+ * key-range parts on different workgroups whose softmax states are merged.  The
+ * decision depends only on the lengths of the non-empty users, n_heads and the
+ * device -- never on zero-length users, max_seqlen, the launch plan or graph
+ * capture -- so those never change the output bits.  Split and whole items agree
+ * within rounding; the worklist entry points below always run items whole.
+ *
+ * Library state.  Each (device, stream) has a worklist buffer with its work
+ * counters and, once a call with max_seqlen > 256 has run, a split-state pool of
+ * about 19 MB.  The first call on a stream that needs more allocates it
+ * (hipMalloc) without synchronising; also during graph capture, when the
+ * allocation is made at once (the thread's capture mode is relaxed for it) and
+ * nothing is recorded into the graph.  A buffer that has to grow is replaced and
+ * the old one kept until the process ends, so graphs captured earlier stay
+ * valid.  Calls on one stream run in stream order and share that state; so does
+ * every graph captured on that stream: replay such a graph in stream order with
+ * the stream's other calls (e.g. on the same stream), never concurrently with
+ * them or with another graph captured on it.  Calls on different streams use
+ * different state and may overlap.
  *   qkv        device, bf16 [T, 3*n_heads*head_dim] (see Layouts)
  *   cu_seqlens device, int32 [num_users+1]
  *   num_users  number of segments U (>= 0)
@@ -102,6 +111,8 @@ enum {
  *   scale      multiplier of q.k before the softmax (1/8 for head_dim 64)
  *   out        device, bf16 [T, n_heads*head_dim]
  *   stream     HIP stream (NULL = default stream)
+ * Errors: the VLCA_ERR_* codes above (VLCA_ERR_WORKSPACE if an allocation
+ * fails); no device work is issued when a call fails its checks.
  */
 int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_users,
                            int max_seqlen, int n_heads, int head_dim, float scale,
@@ -117,10 +128,12 @@ int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t*
 /*
  * Segment scheduler alone (the same device code the forward runs).  Writes, on
  * `stream`, the compact worklist for 64-row q-tiles: items[4*i .. 4*i+3] =
- * (user, q_tile, row_start, length) for i < *count, ordered by q_tile
- * descending and, within one q_tile, by user ascending; users with no rows give
- * no items; entries from *count on are left untouched.  A user's tile count is
- * clamped to ceil(max_seqlen/64).
+ * (user, q_tile, row_start, length) for i < *count.  Order: users grouped by
+ * length class floor(log2(q-tiles of the user)), highest class first; inside a
+ * class, users ascending; a user's items adjacent, from its last q-tile (the
+ * most key tiles) down to q-tile 0.  Users with no rows give no items; entries
+ * from *count on are left untouched.  A user's tile count is clamped to
+ * ceil(max_seqlen/64).
  *   items     device, int32 [capacity][4], caller-owned (may be NULL if capacity
  *             needed is 0)
  *   capacity  items available; must be >= varlen_causal_attn_worklist_capacity()
@@ -146,8 +159,8 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
 /*
  * Which launch plan varlen_causal_attn_fwd uses on the current device for these
  * sizes: writes 1 to *single_kernel when it runs one kernel that orders its own
- * work (no worklist buffer; at most the fixed split-state pool), 0 when it runs
- * the scheduler and the attention kernel over the library workspace.  No device work; queries the
+ * work (no worklist buffer), 0 when it runs the scheduler and the attention
+ * kernel over the stream's worklist.  No device work; queries the
  * device's CU count and the kernel's occupancy once.  Errors as for the size
  * checks of varlen_causal_attn_fwd (VLCA_ERR_HIP without a device).
  */

@@ -2,8 +2,11 @@
 several streams at once.  Every replay, with eager work and synchronisations in
 between, must reproduce the eager output bit for bit; so must every call on a
 stream that runs at the same time as another.  Covers the single-kernel path
-(its split-state pool exists before capture) and the scheduler + worklist path
-(its buffer exists before capture)."""
+and the scheduler + worklist path, with the capture stream's library state
+created before the capture (an eager call first) or during it (a fresh stream),
+and a graph replayed after a larger eager call has replaced its stream's
+worklist."""
+import numpy as np
 import pytest
 import torch
 
@@ -51,6 +54,71 @@ def test_graph_replay_matches_eager(gpu, case):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {rep} differs from the eager result"
+    del g
+
+
+@pytest.mark.parametrize("case", range(len(GRAPH_CASES)))
+def test_graph_captured_on_fresh_stream_matches_eager(gpu, case):
+    """No call on the capture stream before the capture: its worklist and split
+    pool are created during the capture (outside the graph), and the split
+    decision does not depend on that."""
+    name, make = GRAPH_CASES[case]
+    w = make()
+    say(f"[case] graph capture on a fresh stream, {name} ({w.name})")
+    qkv, cu = to_gpu(w)
+    ref = vlca.fwd(qkv, cu, w.max_seqlen, scale=w.scale)  # eager, on the default stream
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    out = torch.zeros((w.total_tokens, 512), dtype=torch.bfloat16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        vlca.fwd(qkv, cu, w.max_seqlen, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager result"
+        with torch.cuda.stream(s):  # eager call on the capture stream between replays
+            again = vlca.fwd(qkv, cu, w.max_seqlen, scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(again, ref)
+    del g
+
+
+def test_graph_replay_after_worklist_growth(gpu):
+    """Capture a small scheduler-plan call, then run a much larger eager call on
+    the same stream (its worklist is replaced by a larger one), then replay: the
+    graph still uses the worklist it was captured with, which is kept."""
+    small = workloads.make_from_lengths(list(np.random.default_rng(41).integers(1, 200, 300)), seed=41)
+    big = workloads.make_config(5)
+    assert not vlca.single_kernel(small.num_users, small.max_seqlen, 8)
+    say("[case] graph replay after the capture stream's worklist grew")
+    qs, cs = to_gpu(small)
+    qb, cb = to_gpu(big)
+    ref_small = vlca.fwd(qs, cs, small.max_seqlen, scale=small.scale)
+    ref_big = vlca.fwd(qb, cb, big.max_seqlen, scale=big.scale)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    out = torch.zeros((small.total_tokens, 512), dtype=torch.bfloat16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        vlca.fwd(qs, cs, small.max_seqlen, scale=small.scale, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            # 1000 users x 64 q-tiles: far more items than the captured worklist holds
+            o_big = vlca.fwd(qb, cb, 262144 if rep == 2 else big.max_seqlen, scale=big.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o_big, ref_big)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_small), f"replay {rep} after growth differs"
     del g
 
 

@@ -96,9 +96,51 @@ def test_zero_length_users_change_nothing(gpu):
     assert torch.equal(base, run_fwd(w2))
 
 
-def test_user_order_permutation(gpu):
-    w = workloads.make_config(3)
-    say("[case] user permutation, config 3")
+def _insert_zeros(lengths, n_zero, seed):
+    """The same users in the same order with n_zero zero-length users at random places."""
+    rng = np.random.default_rng(seed)
+    out = list(lengths)
+    for _ in range(n_zero):
+        out.insert(int(rng.integers(0, len(out) + 1)), 0)
+    return out
+
+
+# A batch whose longest items split into key-range parts.  With 300 zero-length
+# users inserted it has more users than the single-kernel plan takes, so it runs
+# on the scheduler plan; the split decision counts only users with rows, so the
+# bits must not change.
+SPLIT_LENGTHS = [1000, 700, 3, 450, 0, 320]
+
+
+@pytest.mark.parametrize("n_zero", [1, 100, 300, 2000])
+def test_zero_length_users_change_nothing_split_batch(gpu, n_zero):
+    w = workloads.make_from_lengths(SPLIT_LENGTHS, seed=13)
+    L2 = _insert_zeros(SPLIT_LENGTHS, n_zero, seed=n_zero)
+    w2 = workloads.Workload("padded", np.asarray(L2), workloads.cu_from_lengths(L2), w.max_seqlen, w.scale)
+    w2.qkv_bf16 = w.qkv_bf16
+    plans = (vlca.single_kernel(w.num_users, w.max_seqlen, 8), vlca.single_kernel(w2.num_users, w.max_seqlen, 8))
+    say(f"[case] {n_zero} zero-length users inserted into {SPLIT_LENGTHS}; single kernel: {plans}")
+    assert torch.equal(run_fwd(w), run_fwd(w2))
+
+
+def test_zero_length_users_change_nothing_config5(gpu):
+    w = workloads.make_config(5)
+    L2 = _insert_zeros(w.lengths, 500, seed=5)
+    w2 = workloads.Workload("padded", np.asarray(L2), workloads.cu_from_lengths(L2), w.max_seqlen, w.scale)
+    w2.qkv_bf16 = w.qkv_bf16
+    say("[case] 500 zero-length users inserted into config 5")
+    assert torch.equal(run_fwd(w), run_fwd(w2))
+
+
+PERMUTATION_CASES = [("config 3", lambda: workloads.make_config(3)),
+                     ("split batch", lambda: workloads.make_from_lengths(SPLIT_LENGTHS + [900, 17, 600], seed=19))]
+
+
+@pytest.mark.parametrize("case", range(len(PERMUTATION_CASES)))
+def test_user_order_permutation(gpu, case):
+    name, make = PERMUTATION_CASES[case]
+    w = make()
+    say(f"[case] user permutation, {name}")
     base = run_fwd(w)
     perm = np.random.default_rng(5).permutation(w.num_users)
     rows = np.concatenate([np.arange(w.cu_seqlens[u], w.cu_seqlens[u + 1]) for u in perm])
@@ -165,11 +207,11 @@ def test_constant_v(gpu):
 
 # Batches with at most 256 users (and few enough items per workgroup) run as one
 # kernel that locates its own work; larger ones run the scheduler and the
-# attention kernel over a worklist buffer.  For batches of at most 256 users
-# either plan of fwd may split the longest items of users of more than 4 q-tiles
-# into key-range parts, while the explicit worklist path runs every item whole:
-# rows of users that never split agree bit for bit, the others within the parity
-# bound.  Larger batches never split and agree bit for bit.
+# attention kernel over a worklist buffer.  Either plan of fwd may split the
+# longest items of users of more than 4 q-tiles into key-range parts (when the
+# split list fits one round of the grid), while the explicit worklist path runs
+# every item whole: rows of users that never split agree bit for bit, the others
+# within the parity bound.
 WORKLIST_CASES = [
     ("config 2 (single kernel)", lambda: workloads.make_config(2), None),
     ("config 3 (scheduler + worklist)", lambda: workloads.make_config(3), None),
@@ -205,10 +247,7 @@ def test_worklist_entry_point_matches_fwd(gpu, case):
     items, count = vlca.build_worklist(cu, ms)
     b = vlca.fwd_with_worklist(qkv, cu, ms, items, count, n_heads=w.n_heads, scale=w.scale)
     torch.cuda.synchronize()
-    if w.num_users <= 256:
-        assert_same_or_close(a, b.cpu(), w)
-    else:
-        assert torch.equal(a, b.cpu())
+    assert_same_or_close(a, b.cpu(), w)
 
 
 def test_int64_offsets_and_preallocated_out(gpu):

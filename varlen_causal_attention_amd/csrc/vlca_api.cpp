@@ -1,5 +1,5 @@
 // C ABI of the varlen causal attention library: argument checks (all on the
-// host, before any HIP call), the per-(device, stream) scheduler workspace and
+// host, before any HIP call), the per-(device, stream) scheduler worklist and
 // split-state pool, and the launches.  Declarations and the full contract are in
 // include/varlen_causal_attn.h.
 #include <hip/hip_runtime.h>
@@ -10,6 +10,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "varlen_causal_attn.h"
 #include "vlca_internal.h"
@@ -21,29 +22,34 @@ constexpr float kLog2e = 1.4426950408889634f;
 // boundary the work counters (kQueueStride int32 apart).
 constexpr size_t kWorkspaceTail = (1 + vlca::kQueues) * vlca::kQueueStride * sizeof(int32_t);
 
-struct Workspace {
-  int4* items = nullptr;     // capacity items, the int32 count, then the work counters
-  int64_t capacity = 0;
-};
-
-// Key-range splitting in the single-kernel plan: an item of a user of t q-tiles
-// with more than max(ceil(t / 2), kSplitMinWidth) key tiles runs as two parts on
-// different workgroups, when the batch's split list fits in one round of the
-// grid (the kernel decides from the batch's own lengths).  The parts' softmax
-// states meet in a pool of kPoolSlots slots per (device, stream), shared by the
-// heads.
+// Key-range splitting: an item of a user of t q-tiles with more than
+// max(ceil(t / 2), kSplitMinWidth) key tiles runs as two parts on different
+// workgroups, when the batch's split list fits in one round of the single-kernel
+// grid (at most upr units per head; the kernels decide from the lengths of the
+// batch's non-empty users).  The parts' softmax states meet in a pool of
+// vlca::kPoolMaxSlots slots per (device, stream), shared by the heads.
 constexpr int kSplitParts = vlca::kMaxSplitParts;
 constexpr int kSplitMinWidth = 4;
-constexpr int kPoolSlots = 2048;
+constexpr size_t kPoolBytes = static_cast<size_t>(vlca::kPoolMaxSlots) * vlca::kPoolSlotFloats * sizeof(float);
+constexpr size_t kPoolCtrBytes = static_cast<size_t>(vlca::kPoolMaxSlots) * vlca::kSplitCtrStride * sizeof(int32_t);
 
-struct SplitPool {
-  float* pool = nullptr;    // kPoolSlots slots of kPoolSlotFloats floats
-  int32_t* ctr = nullptr;   // kPoolSlots arrival counters, kSplitCtrStride apart
+// Library state of one (device, stream): the scheduler's worklist (capacity
+// items, then the int32 count and the work counters) and the split-state pool
+// (then its arrival counters).  Calls on one stream run in stream order and
+// share it; so does every graph captured on that stream.  Nothing is ever
+// freed: a worklist that has to grow is replaced and the old one kept, since
+// graphs captured earlier may still launch kernels that use it.
+struct StreamState {
+  int4* items = nullptr;
+  int64_t capacity = 0;
+  float* pool = nullptr;
+  int32_t* ctr = nullptr;
 };
 
 std::mutex g_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
-std::map<std::pair<int, hipStream_t>, SplitPool> g_pools;
+std::map<std::pair<int, hipStream_t>, StreamState> g_states;
+std::vector<void*> g_retired;   // replaced worklists, kept for graphs that still refer to them
+std::map<int, hipStream_t> g_zero_streams;  // per device: clears new pools while another stream captures
 std::map<int, int> g_resident;  // 2*device + fused -> resident attention workgroups
 std::map<int, int> g_cus;       // device -> compute units
 
@@ -108,6 +114,14 @@ int grid_size(int dev, int64_t work, bool fused) {
   return static_cast<int>(g);
 }
 
+// Units per head that one round of the single-kernel grid runs (at most the
+// pool's slots per head): a batch splits only if its split list fits.  Depends
+// on the device and n_heads only.
+int split_units_per_round(int dev, int n_heads) {
+  const int g = std::min(grid_size(dev, INT64_MAX, true), vlca::kPoolMaxSlots);
+  return std::max(1, g / n_heads);
+}
+
 // The kernel's `layer_log2` argument.  With every unit in one round of the
 // fixed assignment (at most max_units units per head), log2 of the slots between
 // workgroups that share a CU (workgroups g and g + CUs in launch order; a
@@ -128,64 +142,87 @@ int64_t item_pairs(int num_users, int max_seqlen, int n_heads) {
   return static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen) * n_heads;
 }
 
-// Workspace for (device, stream), grown when a call needs more items.  Growth
-// synchronises `stream` before freeing the old buffer, so it is refused while
-// the stream is capturing.
-int get_workspace(int dev, hipStream_t stream, int64_t capacity, Workspace** out) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  Workspace& ws = g_workspaces[std::make_pair(dev, stream)];
-  if (ws.capacity < capacity) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return VLCA_ERR_HIP;
-    if (st != hipStreamCaptureStatusNone) return VLCA_ERR_WORKSPACE;
-    int64_t cap = ws.capacity > 0 ? ws.capacity : 16384;
-    while (cap < capacity) cap *= 2;
-    if (ws.items != nullptr) {
-      if (hipStreamSynchronize(stream) != hipSuccess) return VLCA_ERR_HIP;
-      (void)hipFree(ws.items);
-      ws.items = nullptr;
-      ws.capacity = 0;
-    }
-    void* p = nullptr;
-    if (hipMalloc(&p, static_cast<size_t>(cap) * sizeof(int4) + kWorkspaceTail) != hipSuccess)
-      return VLCA_ERR_WORKSPACE;
-    ws.items = static_cast<int4*>(p);
-    ws.capacity = cap;
-  }
-  *out = &ws;
+// Whether `stream` is being captured into a graph.
+int capturing(hipStream_t stream, bool* cap) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return VLCA_ERR_HIP;
+  *cap = st != hipStreamCaptureStatusNone;
   return VLCA_OK;
 }
 
-int32_t* workspace_count(const Workspace* ws) { return reinterpret_cast<int32_t*>(ws->items + ws->capacity); }
+// Allocates device memory now, also while a stream is being captured: the
+// calling thread's capture mode is relaxed for the call (an allocation is not a
+// stream operation, so nothing is recorded into the graph).
+hipError_t alloc_now(void** p, size_t bytes) {
+  hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+  if (hipThreadExchangeStreamCaptureMode(&mode) != hipSuccess) return hipErrorUnknown;
+  const hipError_t e = hipMalloc(p, bytes);
+  (void)hipThreadExchangeStreamCaptureMode(&mode);
+  return e;
+}
 
-// Split-state pool for (device, stream), allocated by the first call that splits
-// (fixed size, never grown); its counters are zeroed in stream order before that
-// call and every call leaves them zero.  *capturing = true (and no pool) when it
-// does not exist yet and the stream is being captured: that call runs unsplit.
-int get_split_pool(int dev, hipStream_t stream, SplitPool** out, bool* capturing) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  *capturing = false;
-  SplitPool& sp = g_pools[std::make_pair(dev, stream)];
-  if (sp.pool == nullptr) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return VLCA_ERR_HIP;
-    if (st != hipStreamCaptureStatusNone) {
-      *capturing = true;
-      return VLCA_OK;
-    }
-    const size_t pool_bytes = static_cast<size_t>(kPoolSlots) * vlca::kPoolSlotFloats * sizeof(float);
-    const size_t ctr_bytes = static_cast<size_t>(kPoolSlots) * vlca::kSplitCtrStride * sizeof(int32_t);
-    void* p = nullptr;
-    if (hipMalloc(&p, pool_bytes + ctr_bytes) != hipSuccess) return VLCA_ERR_WORKSPACE;
-    int32_t* ctr = reinterpret_cast<int32_t*>(static_cast<char*>(p) + pool_bytes);
-    if (hipMemsetAsync(ctr, 0, ctr_bytes, stream) != hipSuccess) {
-      (void)hipFree(p);
-      return VLCA_ERR_HIP;
-    }
-    sp.pool = static_cast<float*>(p);
-    sp.ctr = ctr;
+// Zeroes new memory before its first use on `stream`: in stream order, or --
+// while `stream` is being captured, where a memset would be recorded -- on a
+// library stream of the device, waited for here (once per new pool).
+int zero_before_use(int dev, void* p, size_t bytes, hipStream_t stream, bool cap) {
+  if (!cap) return hipMemsetAsync(p, 0, bytes, stream) == hipSuccess ? VLCA_OK : VLCA_ERR_HIP;
+  hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+  if (hipThreadExchangeStreamCaptureMode(&mode) != hipSuccess) return VLCA_ERR_HIP;
+  int rc = VLCA_OK;
+  hipStream_t& zs = g_zero_streams[dev];  // g_mu is held by the caller
+  if (zs == nullptr && hipStreamCreateWithFlags(&zs, hipStreamNonBlocking) != hipSuccess) {
+    zs = nullptr;
+    rc = VLCA_ERR_HIP;
   }
-  *out = &sp;
+  if (rc == VLCA_OK && (hipMemsetAsync(p, 0, bytes, zs) != hipSuccess || hipStreamSynchronize(zs) != hipSuccess))
+    rc = VLCA_ERR_HIP;
+  (void)hipThreadExchangeStreamCaptureMode(&mode);
+  return rc;
+}
+
+// Worklist of (device, stream) with room for `capacity` items.  A larger one
+// replaces it without synchronising the stream; the old one is kept (kernels in
+// flight and captured graphs may still use it).
+int get_workspace(int dev, hipStream_t stream, int64_t capacity, StreamState* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  StreamState& st = g_states[std::make_pair(dev, stream)];
+  if (st.capacity < capacity) {
+    int64_t n = st.capacity > 0 ? st.capacity : 16384;
+    while (n < capacity) n *= 2;
+    void* p = nullptr;
+    if (alloc_now(&p, static_cast<size_t>(n) * sizeof(int4) + kWorkspaceTail) != hipSuccess)
+      return VLCA_ERR_WORKSPACE;
+    if (st.items != nullptr) g_retired.push_back(st.items);
+    st.items = static_cast<int4*>(p);
+    st.capacity = n;
+  }
+  *out = st;
+  return VLCA_OK;
+}
+
+int32_t* workspace_count(const StreamState* st) { return reinterpret_cast<int32_t*>(st->items + st->capacity); }
+
+// Split-state pool of (device, stream), allocated by the first call that may
+// split (fixed size); its arrival counters are zeroed before that call and
+// every call leaves them zero.
+int get_split_pool(int dev, hipStream_t stream, StreamState* out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  StreamState& st = g_states[std::make_pair(dev, stream)];
+  if (st.pool == nullptr) {
+    bool cap = false;
+    if (capturing(stream, &cap) != VLCA_OK) return VLCA_ERR_HIP;
+    void* p = nullptr;
+    if (alloc_now(&p, kPoolBytes + kPoolCtrBytes) != hipSuccess) return VLCA_ERR_WORKSPACE;
+    int32_t* ctr = reinterpret_cast<int32_t*>(static_cast<char*>(p) + kPoolBytes);
+    const int rc = zero_before_use(dev, ctr, kPoolCtrBytes, stream, cap);
+    if (rc != VLCA_OK) {
+      g_retired.push_back(p);  // never freed while a capture may be under way
+      return rc;
+    }
+    st.pool = static_cast<float*>(p);
+    st.ctr = ctr;
+  }
+  *out = st;
   return VLCA_OK;
 }
 
@@ -225,27 +262,23 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
-  // Small batches: one kernel that locates its own work (no worklist buffer).
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   const int64_t pairs = item_pairs(num_users, max_seqlen, n_heads);
-  int grid = grid_size(dev, pairs, true);
-  // Key-range splitting: both plans take the same decision from the batch's own
-  // lengths (split when the list with split items has at most upr units, one
-  // round of the single-kernel grid), so max_seqlen, which picks the plan, does
-  // not change the bits.  Batches of more than kFusedUsers users never split.
+  // Key-range splitting: both plans take the same decision from the lengths of
+  // the batch's non-empty users (split when the list with split items has at
+  // most upr units per head, one round of the single-kernel grid), so neither
+  // max_seqlen (which picks the plan) nor zero-length users change the bits.
   // Only users of more than kSplitMinWidth q-tiles have split items.
-  vlca::SplitArgs split{0, 0, 0, 0, nullptr, nullptr};
-  const int cap = kPoolSlots / n_heads;
-  if (num_users <= vlca::kFusedUsers && max_tiles > kSplitMinWidth && cap >= kSplitParts) {
-    SplitPool* sp = nullptr;
-    bool capturing = false;
-    rc = get_split_pool(dev, stream, &sp, &capturing);
+  vlca::SplitArgs split{0, 0, 0, nullptr, nullptr};
+  const int upr = split_units_per_round(dev, n_heads);
+  if (max_tiles > kSplitMinWidth && upr >= kSplitParts) {
+    StreamState st;
+    rc = get_split_pool(dev, stream, &st);
     if (rc != VLCA_OK) return rc;
-    if (!capturing) {
-      const int upr = std::max(1, grid_size(dev, INT64_MAX, true) / n_heads);
-      split = vlca::SplitArgs{kSplitParts, kSplitMinWidth, upr, cap, sp->pool, sp->ctr};
-    }
+    split = vlca::SplitArgs{kSplitParts, kSplitMinWidth, upr, st.pool, st.ctr};
   }
+  // Small batches: one kernel that locates its own work (no worklist buffer).
+  int grid = grid_size(dev, pairs, true);
   if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
     if (split.p > 1) grid = grid_size(dev, pairs * kSplitParts, true);
     const int layer_log2 = snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
@@ -254,18 +287,13 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
       return VLCA_ERR_HIP;
     return VLCA_OK;
   }
-  // The worklist may hold split units: at most upr more than the whole items.
+  // The worklist holds the whole items, or a split list of at most upr units.
   const int64_t need = required_capacity(num_users, max_seqlen);
-  Workspace* ws = nullptr;
-  rc = get_workspace(dev, stream, split.p > 1 ? need + std::min<int64_t>(need, split.upr) : need, &ws);
-  if (rc == VLCA_ERR_WORKSPACE && split.p > 1) {
-    // E.g. a stream being captured whose workspace only holds whole items: run them whole.
-    split = vlca::SplitArgs{0, 0, 0, 0, nullptr, nullptr};
-    rc = get_workspace(dev, stream, need, &ws);
-  }
+  StreamState st;
+  rc = get_workspace(dev, stream, split.p > 1 ? std::max<int64_t>(need, upr) : need, &st);
   if (rc != VLCA_OK) return rc;
-  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, ws->items, workspace_count(ws),
-                     workspace_count(ws) + vlca::kQueueStride, split, out, stream, true);
+  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, st.items, workspace_count(&st),
+                     workspace_count(&st) + vlca::kQueueStride, split, out, stream, true);
 }
 
 int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity) {
@@ -286,7 +314,7 @@ int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, 
   if (capacity < need) return VLCA_ERR_CAPACITY;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, reinterpret_cast<int4*>(items), count, nullptr,
-                            vlca::SplitArgs{0, 0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
+                            vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
@@ -301,7 +329,7 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale,
                      reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), nullptr,
-                     vlca::SplitArgs{0, 0, 0, 0, nullptr, nullptr}, out, stream, false);
+                     vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, out, stream, false);
 }
 
 int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads, int* single_kernel) {

@@ -18,27 +18,28 @@ constexpr int kMaxGrid = 4096;       // persistent grid cap
 constexpr int kQueues = 8;
 constexpr int kQueueStride = 64;
 
-// Key-range splitting of long items in the single-kernel plan: an item runs as
-// at most kMaxSplitParts parts; each part leaves its softmax state in a pool slot
-// of kPoolSlotFloats floats; one arrival counter per split item, kSplitCtrStride
-// int32 apart, is zero between calls (the last part resets it).
+// Key-range splitting of long items: an item runs as at most kMaxSplitParts
+// parts; each part leaves its softmax state in a pool slot of kPoolSlotFloats
+// floats; one arrival counter per split item, kSplitCtrStride int32 apart, is zero
+// between calls (the last part resets it).  A split list holds at most upr units
+// per head, and upr * n_heads <= kPoolMaxSlots, so every split rank has a slot.
 constexpr int kMaxSplitParts = 2;
 constexpr int kPoolSlotFloats = 4608;  // O: 64 rows x 64 dims, then (m, l) per thread
 constexpr int kSplitCtrStride = 16;
+constexpr int kPoolMaxSlots = 1024;
 
 struct SplitArgs {
   int p;          // 2: split long items in two parts; <= 1: no splitting
   int min_width;  // items of at most this many key tiles always run whole
-  int upr;        // split only if the list with split items holds at most this many units
-  int cap;        // pool slots per head: items whose parts' split ranks reach it run whole
-  float* pool;    // [cap][n_heads] slots
-  int32_t* ctr;   // [cap][n_heads] arrival counters
+  int upr;        // split only if the list with split items holds at most this many units per head
+  float* pool;    // [upr][n_heads] slots
+  int32_t* ctr;   // [upr][n_heads] arrival counters
 };
 
 // Scheduler: one workgroup builds the (user, q_tile, row_start, length) list and,
 // when queue is not null, zeroes the kQueues counters at queue.  split.p == 2:
-// batches of at most 1024 users may get a list of split units (same rule as the
-// single-kernel plan); launch_attention must then get the same split.
+// the list may hold split units (same rule and decision as the single-kernel
+// plan); launch_attention must then get the same split.
 hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles,
                            int4* items, int32_t* count, int32_t* queue, const SplitArgs& split, hipStream_t stream);
 
@@ -58,10 +59,21 @@ hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* c
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
                                   int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
                                   int layer_log2, hipStream_t stream);
-bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid);
 
-// Users the single-kernel plan takes at most (one per lane of four chunks).
+// Users the single-kernel plan takes at most (one per thread of a workgroup),
+// and the rounds of whole items a workgroup can run when it orders the work
+// itself.
 constexpr int kFusedUsers = 256;
+constexpr int kFusedRounds = 16;
+
+// Whether a batch of these sizes runs on the single-kernel plan with this grid.
+inline bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid) {
+  if (num_users > kFusedUsers || grid <= 0) return false;
+  // The prologue's scans carry the item count in 15 bits (and up to twice it in 17).
+  if (num_users * max_tiles > 32767) return false;
+  // rounds = ceil(items * H / grid) when the grid is a multiple of H; items <= users x max q-tiles
+  return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
+}
 
 // Attention workgroups that fit on one CU at once (occupancy of the current device),
 // for the kernel over a worklist or the single-kernel variant.

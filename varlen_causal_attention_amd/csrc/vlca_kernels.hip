@@ -157,7 +157,7 @@ struct OrderScratch {
   int long_off[kThreads];             // ... and their first slots
   int nlong;
   int count;                          // items (units) in the list
-  int n_whole, n_split;               // list sizes without and with key-range splitting
+  int n_whole, n_split;               // any split item; units of the split list (saturated)
 };
 
 // Worklist order: users grouped by length class floor(log2(tiles)), highest
@@ -171,14 +171,15 @@ struct OrderScratch {
 // one item; S.count receives the number of items.  All threads of the
 // workgroup must call this (it contains barriers).
 //
-// Key-range splitting (sp.p > 1, batches of at most kThreads users only): the
-// same rule and decision as the single-kernel plan (split when the list with
-// split items holds at most sp.upr units), so both plans give the same bits.
-// The counts are then carried packed (whole items in the low 15 bits, units in
-// the high 17) and emit(slot, x, y, segment) gets y = q_tile | kind << 16 and x
-// = the user (kind 0, a whole item) or the split rank of the item's first part
-// (kind 1, 2: first / second part; kind 3: a first part that runs nothing).
-// Without splitting, x = user and y = q_tile.
+// Key-range splitting (sp.p > 1): the same rule and decision as the
+// single-kernel plan (split when the list with split items holds at most sp.upr
+// units), taken over every user of the batch; zero-length users add nothing to
+// either count, so they cannot change it.  The counts are then carried packed
+// (whole items in the low 15 bits, units in the high 17: a split list has at most
+// sp.upr <= kMaxGrid units) and emit(slot, x, y, segment) gets y = q_tile | kind
+// << 16 and x = the user (kind 0, a whole item) or the split rank of the item's
+// first part (kind 1, 2: first / second part).  Without splitting, x = user and
+// y = q_tile.
 template <int kThreads, typename CachePtr, typename Emit>
 __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool cached, int nusers, int total,
                             int max_tiles, const SplitArgs& sp, LDS OrderScratch<kThreads>* S, Emit emit) {
@@ -192,19 +193,28 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
   }
   __syncthreads();
   bool split = false;
-  if (sp.p > 1 && nusers <= kThreads) {  // uniform
-    const int t = tid < nusers ? segment_of(cu, s_cu, cached, tid, total, max_tiles).tiles : 0;
-    int w = t, x = t + split_user(t, 1, sp.min_width).split;
+  if (sp.p > 1) {  // uniform
+    // Units of the split list, saturated at sp.upr + 1 (enough to decide), and
+    // whether any item would split at all.
+    const int sat = sp.upr + 1;
+    int x = 0, any = 0;
+    for (int u0 = 0; u0 < nusers; u0 += kThreads) {
+      const int u = u0 + tid;
+      const int t = u < nusers ? segment_of(cu, s_cu, cached, u, total, max_tiles).tiles : 0;
+      const int e = split_user(t, 1, sp.min_width).split;
+      x = min(x + min(t + e, sat), sat);
+      any |= e;
+    }
     for (int o = 32; o > 0; o >>= 1) {
-      w += __shfl_xor(w, o);
-      x += __shfl_xor(x, o);
+      x = min(x + __shfl_xor(x, o), sat);
+      any |= __shfl_xor(any, o);
     }
     if (lane == 0) {
-      __atomic_fetch_add(&S->n_whole, w, __ATOMIC_RELAXED);
-      __atomic_fetch_add(&S->n_split, x, __ATOMIC_RELAXED);
+      __atomic_fetch_add(&S->n_split, x, __ATOMIC_RELAXED);  // <= 16 waves x sat: no overflow
+      __atomic_fetch_or(&S->n_whole, any, __ATOMIC_RELAXED);
     }
     __syncthreads();
-    split = S->n_split > S->n_whole && S->n_split <= sp.upr;
+    split = S->n_whole != 0 && S->n_split <= sp.upr;
   }
   // The count a user adds to the list: its q-tiles, or both counts packed.
   auto units_of_user = [&](int t) {
@@ -256,7 +266,7 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
       pending &= ~__ballot(mine);
     }
     __syncthreads();
-    if (t > 0 && split) {  // at most kThreads users: a single chunk
+    if (t > 0 && split) {
       int both = S->base[cl] + pre;
       for (int w = 0; w < wid; ++w) both += S->wsum[w][cl];
       const int off = both >> 15;
@@ -265,16 +275,10 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
       for (int i = 0; i < t + spl.split; ++i) {
         int nk, k, p;
         unit_of(t, spl, i, nk, k, p);
-        int kind = 0, x = u;
-        if (p > 1) {
-          const int r0 = roff + i - k;  // split ranks r0, r0+1
-          if (r0 + 2 <= sp.cap) {
-            kind = 1 + k;
-            x = r0;
-          } else if (k == 0) {
-            kind = 3;  // pool full: the second part runs the whole item, the first nothing
-          }
-        }
+        // A split item's parts: kind 1 + k, x = split rank r0 of its first part
+        // (ranks r0, r0 + 1 < the list's units <= sp.upr, the pool's slots per head).
+        const int kind = p > 1 ? 1 + k : 0;
+        const int x = p > 1 ? roff + i - k : u;
         emit(off + i, x, (nk - 1) | (kind << 16), s);
       }
     } else if (t > 0) {
@@ -543,11 +547,9 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
 // copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Rounds a workgroup can run when it orders the work itself (kFused), and the
-// most users that path takes (one per thread).  The launch condition counts
-// whole items (kFusedRounds rounds); key-range splitting (below) turns an item
-// into at most kMaxSplitParts work units, so the descriptors hold that many more.
-constexpr int kFusedRounds = 16;
+// The launch condition of the single-kernel plan counts whole items
+// (kFusedRounds rounds); key-range splitting (below) turns an item into at most
+// kMaxSplitParts work units, so the descriptors hold that many more.
 static_assert(kFusedUsers == kAttnThreads, "the shared-list prologue takes one user per thread");
 constexpr int kDescRounds = kFusedRounds * kMaxSplitParts;
 
@@ -593,54 +595,31 @@ __device__ __forceinline__ void store_partial(float* slot, const Lanes& L, const
   store_coherent(slot + 4096 + 2 * threadIdx.x, f32x2{A.m, A.l[0]});
 }
 
-// Run by the last part to finish: fold the states of parts 0 .. parts-1 in that
-// order (its own from registers, the others from their slots, slot_stride floats
-// apart), so the result does not depend on which part finished last.
-__device__ __forceinline__ void merge_parts(const float* slot0, int64_t slot_stride, int parts, int part,
-                                            const Lanes& L, float sl2, Acc& A) {
-  float cm = 0.f, cl = 0.f;
-  f32x4 co[4];
+// Run by the last part to finish (of two): fold the other part's state, read
+// from its slot, into this one's.  The fold is written in part order -- part 0's
+// state times its factor, plus part 1's -- whichever part runs it, so the result
+// does not depend on which part finished last.
+__device__ __forceinline__ void merge_parts(const float* other, int part, const Lanes& L, float sl2, Acc& A) {
+  const f32x2 ml = load_coherent(other + 4096 + 2 * threadIdx.x);
+  const bool first = part == 0;
+  const float m0 = first ? A.m : ml[0], m1 = first ? ml[0] : A.m;
+  const float l0 = first ? A.l[0] : ml[1], l1 = first ? ml[1] : A.l[0];
+  const float mn = fmaxf(m0, m1);
+  const float a = __builtin_amdgcn_exp2f((m0 - mn) * sl2);
+  const float b = __builtin_amdgcn_exp2f((m1 - mn) * sl2);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) co[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < parts; ++k) {
-    float xm, xl;
-    f32x4 xo[4];
-    if (k == part) {
-      xm = A.m;
-      xl = A.l[0];
+  for (int d = 0; d < 4; ++d) {
+    const f32x2 x = load_coherent(other + slot_o_offset(L, d));
+    const f32x2 y = load_coherent(other + slot_o_offset(L, d) + 128);
+    const f32x4 xo = f32x4{x[0], x[1], y[0], y[1]};
 #pragma unroll
-      for (int d = 0; d < 4; ++d) xo[d] = A.o[d];
-    } else {
-      const float* const s = slot0 + k * slot_stride;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f32x2 a = load_coherent(s + slot_o_offset(L, d));
-        const f32x2 b = load_coherent(s + slot_o_offset(L, d) + 128);
-        xo[d] = f32x4{a[0], a[1], b[0], b[1]};
-      }
-      const f32x2 ml = load_coherent(s + 4096 + 2 * threadIdx.x);
-      xm = ml[0];
-      xl = ml[1];
-    }
-    if (k == 0) {
-      cm = xm;
-      cl = xl;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) co[d] = xo[d];
-    } else {
-      const float mn = fmaxf(cm, xm);
-      const float a = __builtin_amdgcn_exp2f((cm - mn) * sl2);
-      const float b = __builtin_amdgcn_exp2f((xm - mn) * sl2);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) co[d] = co[d] * a + xo[d] * b;
-      cl = cl * a + xl * b;
-      cm = mn;
+    for (int r = 0; r < 4; ++r) {
+      const float o0 = first ? A.o[d][r] : xo[r], o1 = first ? xo[r] : A.o[d][r];
+      A.o[d][r] = __builtin_fmaf(o0, a, o1 * b);
     }
   }
-  A.m = cm;
-  A.l[0] = cl;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) A.o[d] = co[d];
+  A.l[0] = __builtin_fmaf(l0, a, l1 * b);
+  A.m = mn;
 }
 
 // kFused = false: walk the first *count items of a worklist built by
@@ -719,8 +698,7 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
   // kFused: the workgroup's unit descriptors (q_tile | kind << 16, row_start,
   // length, head | split rank of part 0 << 16), negative past its last round;
   // shared by the waves, or one copy per wave when each wave orders the users.
-  // kind: 0 the whole item, 1 / 2 its first / second key-range part, 3 nothing
-  // (a first part whose item runs whole as the second).
+  // kind: 0 the whole item, 1 / 2 its first / second key-range part.
   __shared__ i32x4 s_desc[kFused ? kWaves * kDescRounds : 1];
   int desc_base = 0;  // this wave's descriptors: s_desc[desc_base + round]
   __shared__ int s_arrived;
@@ -828,16 +806,8 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
           if constexpr (decltype(with_split)::value) {
             int nk, k, p;
             unit_of(t, spl, i, nk, k, p);
-            int kind = 0, rank0 = 0;
-            if (p > 1) {
-              const int r0 = roff + i - k;  // split ranks r0, r0+1
-              if (r0 + 2 <= sp.cap) {
-                kind = 1 + k;
-                rank0 = r0;
-              } else if (k == 0) {
-                kind = 3;  // pool full: the second part runs the whole item, the first nothing
-              }
-            }
+            const int kind = p > 1 ? 1 + k : 0;
+            const int rank0 = p > 1 ? roff + i - k : 0;  // split ranks rank0, rank0 + 1
             desc[r] = i32x4{(nk - 1) | (kind << 16), sg.start, sg.len, h | (rank0 << 16)};
           } else {
             desc[r] = i32x4{t - 1 - i, sg.start, sg.len, h};
@@ -895,7 +865,6 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       qt = w0 & 0xffff;
       h = w3 & 0xffff;
       const int kind = w0 >> 16;
-      if (kind == 3) continue;  // its item runs whole as the second part
       khi = qt + 1;
       if (kind != 0) {  // key tiles [0, nk/2) or [nk/2, nk)
         parts = 2;
@@ -930,14 +899,6 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       khi = qt + 1;
       if constexpr (kSplit) {
         const int kind = it.y >> 16;  // 0 in a list without split items
-        if (kind == 3) {  // its item runs whole as the second part
-          if (dyn) {      // pass the claim on once every wave has read s_next
-            lds_barrier();
-            if (threadIdx.x == 0) s_next = claimed;
-            lds_barrier();
-          }
-          continue;
-        }
         if (kind != 0) {  // key tiles [0, nk/2) or [nk/2, nk)
           parts = 2;
           part = kind - 1;
@@ -1022,8 +983,9 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
     // j-1, or the Q rows) has been read by every wave, so tile j+1 may refill it.
     // Tile j of the range sits in stage (j - klo) % 2.  Only the diagonal tile
     // (qt, the last tile of the range when khi == qt + 1) needs a mask; the last
-    // tile of a first part goes through the same masked step with nothing masked.
-    const int mlim = (!kSplit || khi == qt + 1) ? L.qr : kTileRows - 1;
+    // tile of a first part takes the unmasked step (a uniform branch: a variable
+    // mask limit cost 14 VGPRs).
+    const bool diag_last = !kSplit || khi == qt + 1;
     int j = klo;
     for (; j + 2 < khi; j += 2) {
       wait_and_barrier<0>();
@@ -1038,10 +1000,16 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       issue_tile(kStageBytes, j + 1);
       tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
       wait_and_barrier<0>();
-      tile_step<true>(st1, L, qf, ones, sl2, rescale_thr, A, mlim);
+      if (diag_last)
+        tile_step<true>(st1, L, qf, ones, sl2, rescale_thr, A, L.qr);
+      else
+        tile_step<false>(st1, L, qf, ones, sl2, rescale_thr, A);
     } else {  // one tile left, in stage 0
       wait_and_barrier<0>();
-      tile_step<true>(st0, L, qf, ones, sl2, rescale_thr, A, mlim);
+      if (diag_last)
+        tile_step<true>(st0, L, qf, ones, sl2, rescale_thr, A, L.qr);
+      else
+        tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
     }
     // The claim made at the item's start is passed on; every wave read s_next
     // before this item's first barrier.
@@ -1065,7 +1033,7 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       }
       lds_barrier();
       if (__builtin_amdgcn_readfirstlane(s_arrived) != parts - 1) continue;
-      merge_parts(slot0, slot_stride, parts, part, L, sl2, A);
+      merge_parts(slot0 + (1 - part) * slot_stride, part, L, sl2, A);
     }
 
     {
@@ -1108,19 +1076,13 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       int layer_log2, float sl2, SplitArgs sp, uint16_t *__restrict__ out
 #define VLCA_ATTENTION_ARGS qkv, items, count, queue, cu, U, max_tiles, n_heads, layer_log2, sl2, sp, out
 
-// Four workgroups per CU (128 VGPRs a lane) is the occupancy the tile step is
-// tuned for.  The split-capable worklist instance needs the occupancy bound to
-// stay there (129 VGPRs without it); on the other instances, which fit anyway,
-// the bound made the compiler schedule the tile step worse (the 25523-token
-// batch 8% slower), so they do without.
+// Four workgroups per CU (at most 128 VGPRs a lane) is the occupancy the tile
+// step is tuned for.  Every instance fits it without an occupancy bound; such a
+// bound made the compiler schedule the tile step worse (the 25523-token batch 8%
+// slower over a worklist).
 template <bool kFused, bool kSplit>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(VLCA_ATTENTION_PARAMS) {
   attention_body<kFused, kSplit>(VLCA_ATTENTION_ARGS);
-}
-
-template <>
-__global__ __launch_bounds__(kAttnThreads, 4) void attention_kernel<false, true>(VLCA_ATTENTION_PARAMS) {
-  attention_body<false, true>(VLCA_ATTENTION_ARGS);
 }
 
 #undef VLCA_ATTENTION_ARGS
@@ -1156,14 +1118,6 @@ hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, in
                      static_cast<const uint16_t*>(qkv), nullptr, nullptr, nullptr, cu_seqlens, num_users, max_tiles,
                      n_heads, layer_log2, scale_log2e, split, static_cast<uint16_t*>(out));
   return hipGetLastError();
-}
-
-bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, int64_t grid) {
-  if (num_users > kFusedUsers || grid <= 0) return false;
-  // The prologue's scans carry the item count in 15 bits (and up to twice it in 17).
-  if (num_users * max_tiles > 32767) return false;
-  // rounds = ceil(items * H / grid) when the grid is a multiple of H; items <= users x max q-tiles
-  return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
 
 int attention_blocks_per_cu(bool fused) {
