@@ -55,6 +55,7 @@ typedef struct ihipStream_t* hipStream_t;
 
 #define VLCA_TILE_ROWS 64          /* query rows per work item, keys per K/V tile  */
 #define VLCA_MAX_SEQLEN 262144     /* max_seqlen upper limit (4096 q-tiles a user) */
+#define VLCA_NOALLOC_MAX_ITEMS 524288  /* worklist items of varlen_causal_attn_fwd_noalloc */
 
 enum {
   VLCA_OK = 0,
@@ -67,7 +68,9 @@ enum {
   VLCA_ERR_CAPACITY = -7,        /* caller worklist buffer smaller than required     */
   VLCA_ERR_ALIAS = -8,           /* qkv and out are the same pointer                 */
   VLCA_ERR_WORKSPACE = -9,       /* library workspace could not be allocated        */
-  VLCA_ERR_HIP = -10             /* a HIP runtime call or kernel launch failed       */
+  VLCA_ERR_HIP = -10,            /* a HIP runtime call or kernel launch failed       */
+  VLCA_ERR_SCRATCH = -11         /* varlen_causal_attn_fwd_noalloc: the batch needs a
+                                    larger worklist than VLCA_NOALLOC_MAX_ITEMS      */
 };
 
 /*
@@ -117,6 +120,27 @@ enum {
 int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_users,
                            int max_seqlen, int n_heads, int head_dim, float scale,
                            void* out, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, serving loops
+ * that forbid hipMalloc): the same computation as varlen_causal_attn_fwd, with
+ * the same launch plan and split decision and hence the same output bits, but
+ * the worklist, work counters and split-state pool live in a fixed scratch array
+ * of about 27 MB per device (loaded with the library's code object; its device
+ * address is looked up once per device on the first call there).  No memory is
+ * allocated and no stream is synchronised.  Every call on a device shares that
+ * device's array, which keeps the last call's contents (the scheduler kernel
+ * re-initialises the counters it needs; the split arrival counters are zero at
+ * load and every call leaves them zero): calls that overlap on one device --
+ * on different streams, or graph replays beside other calls -- race and must
+ * not be made.  Limit: a batch on the scheduler plan (varlen_causal_attn_single_kernel()
+ * gives 0) must need at most VLCA_NOALLOC_MAX_ITEMS worklist items
+ * (num_users*ceil(max_seqlen/64)), else VLCA_ERR_SCRATCH before any device work.
+ * Arguments, layouts and other errors as for varlen_causal_attn_fwd.
+ */
+int varlen_causal_attn_fwd_noalloc(const void* qkv, const int32_t* cu_seqlens, int num_users,
+                                   int max_seqlen, int n_heads, int head_dim, float scale,
+                                   void* out, hipStream_t stream);
 
 /*
  * Worklist size (in items) needed by varlen_causal_attn_build_worklist and

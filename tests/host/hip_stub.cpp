@@ -134,4 +134,11 @@ hipError_t launch_attention_fused(const void*, const int32_t*, int num_users, in
 
 int attention_blocks_per_cu(bool) { return g.blocks_per_cu; }
 
+hipError_t noalloc_scratch(char** ptr) {
+  static char* scratch = static_cast<char*>(std::calloc(kNoAllocScratchBytes, 1));
+  ++g.scratch_lookups;
+  *ptr = scratch;
+  return scratch != nullptr ? hipSuccess : hipErrorOutOfMemory;
+}
+
 }  // namespace vlca

@@ -31,7 +31,7 @@ struct State {
   hipStream_t capturing = nullptr;             // the stream being captured (global mode), if any
   hipStreamCaptureMode mode = hipStreamCaptureModeGlobal;  // this thread's capture mode
   int allocs = 0, frees = 0, syncs = 0, streams_created = 0;
-  int memsets = 0, captured_memsets = 0, capture_violations = 0, dirty_counters = 0;
+  int memsets = 0, captured_memsets = 0, capture_violations = 0, dirty_counters = 0, scratch_lookups = 0;
   std::vector<hipStream_t> synced;
   std::vector<Launch> launches;
 };

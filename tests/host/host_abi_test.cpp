@@ -137,11 +137,46 @@ static void test_state_created_during_capture() {
   CHECK(fwd(306, 1000, 8, s) == VLCA_OK && g.allocs == 3 && g.dirty_counters == 0);
 }
 
+static void test_noalloc_entry_point() {
+  stub::reset();
+  const hipStream_t s = stream_id(9);
+  char* scratch = nullptr;
+  CHECK(vlca::noalloc_scratch(&scratch) == hipSuccess);
+  stub::reset();
+  auto na = [&](int users, int ms, int heads) {
+    return varlen_causal_attn_fwd_noalloc(QKV, CU, users, ms, heads, 64, 0.125f, OUT, s);
+  };
+  // Single-kernel plan with split settings: the pool is the scratch array's start.
+  CHECK(na(60, 452, 8) == VLCA_OK);
+  CHECK(g.launches.size() == 1 && g.launches[0].kind == 'f' && g.launches[0].split.p == 2);
+  CHECK(reinterpret_cast<char*>(g.launches[0].split.pool) == scratch);
+  CHECK(reinterpret_cast<char*>(g.launches[0].split.ctr) == scratch + vlca::kNoAllocPoolBytes);
+  // Scheduler plan: the worklist sits after the pool, its count after the items.
+  CHECK(na(1000, 4096, 8) == VLCA_OK);
+  CHECK(g.launches.size() == 3 && g.launches[1].kind == 's' && g.launches[2].kind == 'a');
+  CHECK(reinterpret_cast<const char*>(g.launches[1].items) == scratch + vlca::kNoAllocItemsOffset);
+  CHECK(g.launches[1].touched == vlca::kNoAllocItems * 16 + 4);
+  CHECK(g.launches[2].split.upr == 128);
+  // Too large for the scratch worklist: refused before any device work.
+  const size_t before = g.launches.size();
+  CHECK(na(VLCA_NOALLOC_MAX_ITEMS / 64 + 1, 4096, 8) == VLCA_ERR_SCRATCH);
+  CHECK(na(VLCA_NOALLOC_MAX_ITEMS / 64, 4096, 8) == VLCA_OK);
+  CHECK(g.launches.size() == before + 2);
+  // Argument errors as for fwd.
+  CHECK(na(4, 64, 0) == VLCA_ERR_N_HEADS && na(-1, 64, 8) == VLCA_ERR_NEGATIVE_SIZE);
+  // Never allocates, frees, synchronises or sets memory -- captured or not.
+  g.capturing = s;
+  CHECK(na(306, 1000, 8) == VLCA_OK && na(60, 452, 8) == VLCA_OK);
+  g.capturing = nullptr;
+  CHECK(g.allocs == 0 && g.frees == 0 && g.syncs == 0 && g.memsets == 0 && g.capture_violations == 0);
+}
+
 int main() {
   test_argument_errors();
   test_plans_and_split_settings();
   test_worklist_growth_keeps_old_buffers();
   test_state_created_during_capture();
+  test_noalloc_entry_point();
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
 }

@@ -13,7 +13,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "VlcaError", "library", "library_path", "fwd", "build_worklist", "fwd_with_worklist",
+    "VlcaError", "library", "library_path", "fwd", "fwd_noalloc", "build_worklist", "fwd_with_worklist",
     "worklist_capacity", "single_kernel", "tile_rows", "strerror", "call_module", "EXPORTED_SYMBOLS",
 ]
 
@@ -24,6 +24,7 @@ _call = None  # the CPython trampoline for fwd / fwd_worklist (ctypes when it is
 
 EXPORTED_SYMBOLS = (
     "varlen_causal_attn_fwd",
+    "varlen_causal_attn_fwd_noalloc",
     "varlen_causal_attn_worklist_capacity",
     "varlen_causal_attn_build_worklist",
     "varlen_causal_attn_fwd_worklist",
@@ -55,6 +56,8 @@ def library():
     c_int, c_float = ctypes.c_int, ctypes.c_float
     lib.varlen_causal_attn_fwd.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
     lib.varlen_causal_attn_fwd.restype = c_int
+    lib.varlen_causal_attn_fwd_noalloc.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
+    lib.varlen_causal_attn_fwd_noalloc.restype = c_int
     lib.varlen_causal_attn_worklist_capacity.argtypes = [c_int, c_int, i64p]
     lib.varlen_causal_attn_worklist_capacity.restype = c_int
     lib.varlen_causal_attn_build_worklist.argtypes = [i32p, c_int, c_int, i32p, ctypes.c_int64, i32p, vp]
@@ -183,6 +186,32 @@ def fwd(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
     rc = _call.fwd(*args) if _call is not None else lib.varlen_causal_attn_fwd(*args)
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd")
+    return out
+
+
+def fwd_noalloc(qkv, cu_seqlens, max_seqlen: int, out, n_heads: int = 8, head_dim: int = 64,
+                scale: Optional[float] = None):
+    """:func:`fwd` through ``varlen_causal_attn_fwd_noalloc``: same bits, no allocation in the library.
+
+    ``out`` must be given (this call allocates nothing, torch included) and
+    ``cu_seqlens`` must already be an int32 device tensor.  Calls that overlap
+    on one device race on the library's fixed scratch array.
+    """
+    torch = _torch_mod()
+    _check_qkv(qkv, n_heads, head_dim)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1 \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
+    if out is None:
+        raise ValueError("fwd_noalloc needs a preallocated out tensor")
+    out = _out_tensor(qkv, n_heads, head_dim, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    rc = library().varlen_causal_attn_fwd_noalloc(qkv.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.shape[0] - 1,
+                                                  int(max_seqlen), int(n_heads), int(head_dim), float(scale),
+                                                  out.data_ptr(), _stream_handle(qkv.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_fwd_noalloc")
     return out
 
 

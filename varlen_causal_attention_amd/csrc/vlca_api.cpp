@@ -296,6 +296,43 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
                      workspace_count(&st) + vlca::kQueueStride, split, out, stream, true);
 }
 
+int varlen_causal_attn_fwd_noalloc(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
+                                   int n_heads, int head_dim, float scale, void* out, hipStream_t stream) {
+  int rc = check_attention_args(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out);
+  if (rc != VLCA_OK) return rc;
+  if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  const int64_t pairs = item_pairs(num_users, max_seqlen, n_heads);
+  const int upr = split_units_per_round(dev, n_heads);
+  const bool may_split = max_tiles > kSplitMinWidth && upr >= kSplitParts;
+  int grid = grid_size(dev, pairs, true);
+  const bool fused = vlca::fused_fits(num_users, max_tiles, n_heads, grid);
+  // The same plan and split settings as varlen_causal_attn_fwd, over the
+  // device's scratch array instead of the stream's state.
+  const int64_t need = required_capacity(num_users, max_seqlen);
+  if (!fused && (may_split ? std::max<int64_t>(need, upr) : need) > vlca::kNoAllocItems) return VLCA_ERR_SCRATCH;
+  char* base = nullptr;
+  if (vlca::noalloc_scratch(&base) != hipSuccess) return VLCA_ERR_HIP;
+  vlca::SplitArgs split{0, 0, 0, nullptr, nullptr};
+  if (may_split)
+    split = vlca::SplitArgs{kSplitParts, kSplitMinWidth, upr, reinterpret_cast<float*>(base),
+                            reinterpret_cast<int32_t*>(base + vlca::kNoAllocPoolBytes)};
+  if (fused) {
+    if (split.p > 1) grid = grid_size(dev, pairs * kSplitParts, true);
+    const int layer_log2 = snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
+    if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, split, out,
+                                     grid, layer_log2, stream) != hipSuccess)
+      return VLCA_ERR_HIP;
+    return VLCA_OK;
+  }
+  int4* items = reinterpret_cast<int4*>(base + vlca::kNoAllocItemsOffset);
+  int32_t* count = reinterpret_cast<int32_t*>(items + vlca::kNoAllocItems);
+  return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, items, count,
+                     count + vlca::kQueueStride, split, out, stream, true);
+}
+
 int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity) {
   int rc = check_sizes(num_users, max_seqlen);
   if (rc != VLCA_OK) return rc;
@@ -360,6 +397,7 @@ const char* varlen_causal_attn_strerror(int code) {
     case VLCA_ERR_ALIAS: return "qkv and out must not be the same buffer";
     case VLCA_ERR_WORKSPACE: return "library workspace could not be allocated (or must grow during stream capture)";
     case VLCA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case VLCA_ERR_SCRATCH: return "batch needs more worklist items than the no-allocation scratch holds";
     default: return "unknown error code";
   }
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "varlen_causal_attn.h"
+
 namespace vlca {
 
 constexpr int kTileRows = 64;        // query rows per work item == keys per K/V tile
@@ -74,6 +76,22 @@ inline bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, in
   // rounds = ceil(items * H / grid) when the grid is a multiple of H; items <= users x max q-tiles
   return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
+
+// Scratch memory of the no-allocation entry point: one fixed array per device
+// (file-scope in vlca_noalloc.hip), laid out as the split pool, its arrival
+// counters, then a worklist of kNoAllocItems items followed by its count and
+// work counters.
+constexpr int64_t kNoAllocItems = VLCA_NOALLOC_MAX_ITEMS;
+constexpr size_t kNoAllocPoolBytes = size_t(kPoolMaxSlots) * kPoolSlotFloats * sizeof(float);
+constexpr size_t kNoAllocCtrBytes = size_t(kPoolMaxSlots) * kSplitCtrStride * sizeof(int32_t);
+constexpr size_t kNoAllocItemsOffset = kNoAllocPoolBytes + kNoAllocCtrBytes;
+constexpr size_t kNoAllocTailBytes = size_t(1 + kQueues) * kQueueStride * sizeof(int32_t);
+constexpr size_t kNoAllocScratchBytes = kNoAllocItemsOffset + size_t(kNoAllocItems) * 16 + kNoAllocTailBytes;
+
+// Device address of the current device's scratch array (looked up once per
+// device with hipGetSymbolAddress; the array's host-side name is no device
+// address).
+hipError_t noalloc_scratch(char** ptr);
 
 // Attention workgroups that fit on one CU at once (occupancy of the current device),
 // for the kernel over a worklist or the single-kernel variant.

@@ -316,8 +316,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
                                                                  int max_tiles, int4* __restrict__ items,
                                                                  int32_t* __restrict__ count,
                                                                  int32_t* __restrict__ queue, SplitArgs sp) {
-  // The attention kernel's work counters start at zero.
+  // The attention kernel's work counters start at zero; so do the split pool's
+  // arrival counters (every call also leaves them zero).
   if (queue != nullptr && threadIdx.x < kQueues) queue[threadIdx.x * kQueueStride] = 0;
+  if (sp.p > 1)
+    for (int i = threadIdx.x; i < kPoolMaxSlots; i += kSchedThreads) sp.ctr[i * kSplitCtrStride] = 0;
   __shared__ int s_cu_lds[kSchedCache + 1];
   __shared__ OrderScratch<kSchedThreads> S_lds;
   LDS int* const s_cu = (LDS int*)s_cu_lds;
