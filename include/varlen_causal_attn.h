@@ -69,8 +69,10 @@ enum {
   VLCA_ERR_ALIAS = -8,           /* qkv and out are the same pointer                 */
   VLCA_ERR_WORKSPACE = -9,       /* library workspace could not be allocated        */
   VLCA_ERR_HIP = -10,            /* a HIP runtime call or kernel launch failed       */
-  VLCA_ERR_SCRATCH = -11         /* varlen_causal_attn_fwd_noalloc: the batch needs a
+  VLCA_ERR_SCRATCH = -11,        /* varlen_causal_attn_fwd_noalloc: the batch needs a
                                     larger worklist than VLCA_NOALLOC_MAX_ITEMS      */
+  VLCA_ERR_BUCKETS = -12         /* runner bucket sizes not positive and increasing,
+                                    or more than 64 buckets                          */
 };
 
 /*
@@ -189,6 +191,61 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
  * checks of varlen_causal_attn_fwd (VLCA_ERR_HIP without a device).
  */
 int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads, int* single_kernel);
+
+/*
+ * Bucketed graph runner (cti2026 README, CUDA Graph section: bucketed padding,
+ * fixed attention grid, no host synchronisation, variable number of users).
+ * Packed batches of varying size replay one of a few captured HIP graphs:
+ *   - bucket b holds up to bucket_tokens[b] tokens (strictly increasing, e.g.
+ *     2560, 3072, ..., 7168); a batch of T tokens uses the smallest bucket with
+ *     T <= bucket_tokens[b], whose graph runs the forward over the static buffers
+ *     with the constant max_seqlen = bucket_tokens[b];
+ *   - the offsets have a fixed length max_users + 1: a batch with fewer users is
+ *     padded on the device with zero-length users (no host read of device data);
+ *   - a batch above the top bucket, or with more than max_users users, runs the
+ *     eager forward instead (with the caller's max_seqlen);
+ *   - every bucket's graph is captured at creation (precapture != 0) or on its
+ *     first use.
+ * The output equals varlen_causal_attn_fwd's on the same batch bit for bit (the
+ * forward's result does not depend on max_seqlen or zero-length users).
+ *
+ * qkv_static, out_static: caller-owned device buffers of at least top-bucket rows
+ * of the qkv and out layouts, kept alive until the runner is destroyed; the graphs
+ * read and write them.  A producer may write a batch's qkv rows straight into
+ * qkv_static and read the result from out_static (run() then copies nothing);
+ * other buffers are copied in and out on the stream.  The runner owns the
+ * padded offsets and a stream of its own on which it captures (its graphs share
+ * that stream's library state); graphs are launched on run()'s stream.  A
+ * runner is used on one stream at a time; runs on it are ordered by that stream.
+ * create() synchronises the device once (clearing the offsets) and allocates;
+ * run() allocates only when it captures a bucket lazily.
+ */
+typedef struct vlca_graph_runner vlca_graph_runner;
+
+int varlen_causal_attn_runner_create(const int32_t* bucket_tokens, int n_buckets, int max_users, int n_heads,
+                                     float scale, void* qkv_static, void* out_static, int precapture,
+                                     vlca_graph_runner** runner);
+
+/*
+ * Runs one batch: qkv, cu_seqlens (num_users + 1 offsets), out as for
+ * varlen_causal_attn_fwd, total_tokens = cu_seqlens[num_users] (host value; it
+ * picks the bucket, and offsets are clamped to it on the device), max_seqlen
+ * for the eager fallback.  *bucket_used (may be NULL) receives the bucket index
+ * or -1 for the eager path.  Asynchronous on `stream`.
+ */
+int varlen_causal_attn_runner_run(vlca_graph_runner* runner, const void* qkv, const int32_t* cu_seqlens,
+                                  int num_users, int total_tokens, int max_seqlen, void* out, hipStream_t stream,
+                                  int* bucket_used);
+
+/* The bucket a batch would use (-1: the eager path).  Host arithmetic only. */
+int varlen_causal_attn_runner_bucket(const vlca_graph_runner* runner, int num_users, int total_tokens, int* bucket);
+
+/* Number of buckets whose graph has been captured. */
+int varlen_causal_attn_runner_captured(const vlca_graph_runner* runner, int* n_captured);
+
+/* Waits for the device, then frees the graphs, the offsets and the capture
+ * stream (not the caller's static buffers).  NULL is a no-op. */
+int varlen_causal_attn_runner_destroy(vlca_graph_runner* runner);
 
 /* Query rows per work item (and keys per K/V tile): VLCA_TILE_ROWS. */
 int varlen_causal_attn_tile_rows(void);

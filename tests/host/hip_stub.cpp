@@ -75,8 +75,12 @@ hipError_t hipMemsetAsync(void* p, int v, size_t n, hipStream_t s) {
 }
 
 hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
-  static char fake[16];
-  *s = reinterpret_cast<hipStream_t>(&fake[++g.streams_created % 16]);
+  // Distinct handles for the whole run (the library keys its state by stream).
+  static char fake[64];
+  static int next = 0;
+  if (next == 64) return hipErrorOutOfMemory;
+  *s = reinterpret_cast<hipStream_t>(&fake[next++]);
+  ++g.streams_created;
   return hipSuccess;
 }
 
@@ -90,9 +94,82 @@ hipError_t hipStreamSynchronize(hipStream_t s) {
   return hipSuccess;
 }
 
+hipError_t hipMemset(void* p, int v, size_t n) {
+  if (g.capturing != nullptr && g.mode != hipStreamCaptureModeRelaxed) {
+    ++g.capture_violations;
+    return hipErrorStreamCaptureUnsupported;
+  }
+  std::memset(p, v, n);
+  ++g.memsets;
+  return hipSuccess;
+}
+
+hipError_t hipMemcpyAsync(void*, const void*, size_t n, hipMemcpyKind, hipStream_t s) {
+  if (g.capturing != nullptr && s == g.capturing) ++g.captured_memsets;
+  ++g.copies;
+  g.copied_bytes += static_cast<int64_t>(n);
+  return hipSuccess;
+}
+
+hipError_t hipStreamDestroy(hipStream_t) {
+  ++g.streams_destroyed;
+  return hipSuccess;
+}
+
+hipError_t hipDeviceSynchronize() {
+  ++g.device_syncs;
+  return hipSuccess;
+}
+
+hipError_t hipStreamBeginCapture(hipStream_t s, hipStreamCaptureMode) {
+  if (g.capturing != nullptr) return hipErrorIllegalState;
+  g.capturing = s;
+  return hipSuccess;
+}
+
+hipError_t hipStreamEndCapture(hipStream_t s, hipGraph_t* graph) {
+  if (g.capturing != s) return hipErrorIllegalState;
+  g.capturing = nullptr;
+  ++g.captures;
+  *graph = reinterpret_cast<hipGraph_t>(new int(g.captures));
+  return hipSuccess;
+}
+
+hipError_t hipGraphInstantiate(hipGraphExec_t* exec, hipGraph_t graph, hipGraphNode_t*, char*, size_t) {
+  *exec = reinterpret_cast<hipGraphExec_t>(new int(*reinterpret_cast<int*>(graph)));
+  return hipSuccess;
+}
+
+hipError_t hipGraphLaunch(hipGraphExec_t exec, hipStream_t s) {
+  ++g.graph_launches;
+  g.launches.push_back({'g', nullptr, *reinterpret_cast<int*>(exec), 0, 0, 0, 0, -1, {0, 0, 0, nullptr, nullptr}, s});
+  return hipSuccess;
+}
+
+hipError_t hipGraphExecDestroy(hipGraphExec_t exec) {
+  delete reinterpret_cast<int*>(exec);
+  ++g.execs_destroyed;
+  return hipSuccess;
+}
+
+hipError_t hipGraphDestroy(hipGraph_t graph) {
+  delete reinterpret_cast<int*>(graph);
+  ++g.graphs_destroyed;
+  return hipSuccess;
+}
+
 }  // extern "C"
 
 namespace vlca {
+
+hipError_t launch_pad_offsets(const int32_t*, int num_users, int total, int32_t*, int max_users, hipStream_t) {
+  ++g.pads;
+  g.last_pad_users = num_users;
+  g.last_pad_total = total;
+  g.last_pad_max = max_users;
+  return hipSuccess;
+}
+
 
 namespace {
 int64_t touch(const int4* items, const int32_t* count) {

@@ -16,7 +16,7 @@
 namespace stub {
 
 struct Launch {
-  char kind;  // 's' scheduler, 'a' attention over a worklist, 'f' single kernel
+  char kind;  // 's' scheduler, 'a' attention over a worklist, 'f' single kernel, 'g' graph launch
   const void* items;
   int64_t touched;  // bytes of `items` the stand-in kernel wrote
   int num_users, max_tiles, n_heads, grid, layer_log2;
@@ -32,6 +32,10 @@ struct State {
   hipStreamCaptureMode mode = hipStreamCaptureModeGlobal;  // this thread's capture mode
   int allocs = 0, frees = 0, syncs = 0, streams_created = 0;
   int memsets = 0, captured_memsets = 0, capture_violations = 0, dirty_counters = 0, scratch_lookups = 0;
+  int captures = 0, graph_launches = 0, graphs_destroyed = 0, execs_destroyed = 0, copies = 0, pads = 0;
+  int device_syncs = 0, streams_destroyed = 0;
+  int64_t copied_bytes = 0;
+  int last_pad_users = -1, last_pad_total = -1, last_pad_max = -1;
   std::vector<hipStream_t> synced;
   std::vector<Launch> launches;
 };

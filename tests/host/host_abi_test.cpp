@@ -171,12 +171,81 @@ static void test_noalloc_entry_point() {
   CHECK(g.allocs == 0 && g.frees == 0 && g.syncs == 0 && g.memsets == 0 && g.capture_violations == 0);
 }
 
+static void test_graph_runner() {
+  stub::reset();
+  static char qkv_static[16], out_static[16];
+  const int32_t pages[10] = {2560, 3072, 3584, 4096, 4608, 5120, 5632, 6144, 6656, 7168};
+  vlca_graph_runner* r = nullptr;
+  // Argument checks before any HIP call.
+  const int32_t bad1[3] = {2560, 2560, 3072}, bad2[2] = {0, 64}, big[1] = {VLCA_MAX_SEQLEN + 1};
+  CHECK(varlen_causal_attn_runner_create(bad1, 3, 20, 8, 0.125f, qkv_static, out_static, 1, &r) == VLCA_ERR_BUCKETS);
+  CHECK(varlen_causal_attn_runner_create(bad2, 2, 20, 8, 0.125f, qkv_static, out_static, 1, &r) == VLCA_ERR_BUCKETS);
+  CHECK(varlen_causal_attn_runner_create(pages, 0, 20, 8, 0.125f, qkv_static, out_static, 1, &r) == VLCA_ERR_BUCKETS);
+  CHECK(varlen_causal_attn_runner_create(big, 1, 20, 8, 0.125f, qkv_static, out_static, 1, &r) == VLCA_ERR_TOO_LARGE);
+  CHECK(varlen_causal_attn_runner_create(pages, 10, 0, 8, 0.125f, qkv_static, out_static, 1, &r) ==
+        VLCA_ERR_NEGATIVE_SIZE);
+  CHECK(varlen_causal_attn_runner_create(pages, 10, 20, 8, 0.125f, nullptr, out_static, 1, &r) ==
+        VLCA_ERR_NULL_POINTER);
+  CHECK(varlen_causal_attn_runner_create(pages, 10, 20, 8, 0.125f, qkv_static, qkv_static, 1, &r) == VLCA_ERR_ALIAS);
+  CHECK(r == nullptr && g.allocs == 0 && g.launches.empty());
+
+  // Pre-capture: one graph per bucket, each the forward with 20 users and
+  // max_seqlen = the bucket, captured on the runner's own stream; nothing runs.
+  CHECK(varlen_causal_attn_runner_create(pages, 10, 20, 8, 0.125f, qkv_static, out_static, 1, &r) == VLCA_OK);
+  CHECK(r != nullptr && g.captures == 10 && g.graph_launches == 0 && g.capture_violations == 0);
+  int n = 0;
+  CHECK(varlen_causal_attn_runner_captured(r, &n) == VLCA_OK && n == 10);
+  const hipStream_t cap_stream = g.launches.front().stream;
+  for (const auto& l : g.launches) CHECK(l.stream == cap_stream && l.kind != 'g');
+  CHECK(g.launches[0].kind == 'f' && g.launches[0].num_users == 20 && g.launches[0].max_tiles == 40);
+  CHECK(g.launches.back().kind == 'a');  // 20 users x 112 tiles x 8 heads: the scheduler plan
+  int b = -2;
+  CHECK(varlen_causal_attn_runner_bucket(r, 20, 2560, &b) == VLCA_OK && b == 0);
+  CHECK(varlen_causal_attn_runner_bucket(r, 20, 2561, &b) == VLCA_OK && b == 1);
+  CHECK(varlen_causal_attn_runner_bucket(r, 3, 7168, &b) == VLCA_OK && b == 9);
+  CHECK(varlen_causal_attn_runner_bucket(r, 3, 7169, &b) == VLCA_OK && b == -1);
+  CHECK(varlen_causal_attn_runner_bucket(r, 21, 100, &b) == VLCA_OK && b == -1);
+
+  // A batch of 3000 tokens and 15 users: bucket 1, offsets padded to 20 users on the
+  // device, qkv copied in and out copied back (the caller's own buffers), graph replayed.
+  const hipStream_t s = stream_id(10);
+  g.launches.clear();
+  CHECK(varlen_causal_attn_runner_run(r, QKV, CU, 15, 3000, 452, OUT, s, &b) == VLCA_OK && b == 1);
+  CHECK(g.pads == 1 && g.last_pad_users == 15 && g.last_pad_total == 3000 && g.last_pad_max == 20);
+  CHECK(g.copies == 2 && g.copied_bytes == int64_t(3000) * (1536 + 512) * 2);
+  CHECK(g.launches.size() == 1 && g.launches[0].kind == 'g' && g.launches[0].stream == s);
+  CHECK(g.launches[0].touched == 2);  // the second bucket's graph
+  // The static buffers themselves: nothing copied.
+  CHECK(varlen_causal_attn_runner_run(r, qkv_static, CU, 20, 2560, 452, out_static, s, &b) == VLCA_OK && b == 0);
+  CHECK(g.copies == 2 && g.graph_launches == 2);
+  // Above the top bucket, or too many users: the eager forward on the caller's stream.
+  g.launches.clear();
+  CHECK(varlen_causal_attn_runner_run(r, QKV, CU, 60, 9000, 1024, OUT, s, &b) == VLCA_OK && b == -1);
+  CHECK(g.launches.size() == 1 && g.launches[0].kind == 'f' && g.launches[0].stream == s);
+  CHECK(g.launches[0].max_tiles == 16 && g.graph_launches == 2);
+  CHECK(varlen_causal_attn_runner_run(r, QKV, CU, 21, 100, 100, OUT, s, &b) == VLCA_OK && b == -1);
+  CHECK(varlen_causal_attn_runner_destroy(r) == VLCA_OK);
+  CHECK(g.execs_destroyed == 10 && g.graphs_destroyed == 10 && g.device_syncs == 1 && g.streams_destroyed == 1);
+
+  // Lazy capture: a bucket's graph is captured on its first use only.
+  stub::reset();
+  CHECK(varlen_causal_attn_runner_create(pages, 10, 20, 8, 0.125f, qkv_static, out_static, 0, &r) == VLCA_OK);
+  CHECK(varlen_causal_attn_runner_captured(r, &n) == VLCA_OK && n == 0 && g.captures == 0);
+  CHECK(varlen_causal_attn_runner_run(r, QKV, CU, 15, 5000, 452, OUT, s, &b) == VLCA_OK && b == 5);
+  CHECK(varlen_causal_attn_runner_run(r, QKV, CU, 15, 4700, 452, OUT, s, &b) == VLCA_OK && b == 5);
+  CHECK(varlen_causal_attn_runner_captured(r, &n) == VLCA_OK && n == 1 && g.captures == 1 && g.graph_launches == 2);
+  CHECK(g.capture_violations == 0);
+  CHECK(varlen_causal_attn_runner_destroy(r) == VLCA_OK && varlen_causal_attn_runner_destroy(nullptr) == VLCA_OK);
+}
+
 int main() {
+  setvbuf(stdout, nullptr, _IONBF, 0);
   test_argument_errors();
   test_plans_and_split_settings();
   test_worklist_growth_keeps_old_buffers();
   test_state_created_during_capture();
   test_noalloc_entry_point();
+  test_graph_runner();
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
 }

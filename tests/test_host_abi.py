@@ -4,7 +4,10 @@
 against a stand-in HIP runtime (``tests/host/hip_stub.cpp``): argument errors,
 the launch plan and split settings, and the per-stream worklist and split-pool
 bookkeeping (no stream synchronisation, nothing freed that a captured graph may
-still use, state created during a capture without recording into it).
+still use, state created during a capture without recording into it), the
+no-allocation entry point's scratch layout, and the bucketed graph runner
+(bucket choice, pre-capture and lazy capture, device-side offset padding,
+eager fallback).
 """
 import os
 import shutil
@@ -15,7 +18,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HOST = os.path.join(ROOT, "tests", "host")
 SOURCES = [os.path.join(HOST, "host_abi_test.cpp"), os.path.join(HOST, "hip_stub.cpp"),
-           os.path.join(ROOT, "varlen_causal_attention_amd", "csrc", "vlca_api.cpp")]
+           os.path.join(ROOT, "varlen_causal_attention_amd", "csrc", "vlca_api.cpp"),
+           os.path.join(ROOT, "varlen_causal_attention_amd", "csrc", "vlca_graph.cpp")]
 
 
 def test_host_abi_under_sanitizers(tmp_path):

@@ -15,6 +15,7 @@ from typing import Optional, Tuple
 __all__ = [
     "VlcaError", "library", "library_path", "fwd", "fwd_noalloc", "build_worklist", "fwd_with_worklist",
     "worklist_capacity", "single_kernel", "tile_rows", "strerror", "call_module", "EXPORTED_SYMBOLS",
+    "GraphRunner", "PAGES_BUCKETS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +30,11 @@ EXPORTED_SYMBOLS = (
     "varlen_causal_attn_build_worklist",
     "varlen_causal_attn_fwd_worklist",
     "varlen_causal_attn_single_kernel",
+    "varlen_causal_attn_runner_create",
+    "varlen_causal_attn_runner_run",
+    "varlen_causal_attn_runner_bucket",
+    "varlen_causal_attn_runner_captured",
+    "varlen_causal_attn_runner_destroy",
     "varlen_causal_attn_tile_rows",
     "varlen_causal_attn_strerror",
 )
@@ -67,6 +73,18 @@ def library():
     lib.varlen_causal_attn_fwd_worklist.restype = c_int
     lib.varlen_causal_attn_single_kernel.argtypes = [c_int, c_int, c_int, ctypes.POINTER(ctypes.c_int)]
     lib.varlen_causal_attn_single_kernel.restype = c_int
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.varlen_causal_attn_runner_create.argtypes = [ctypes.POINTER(ctypes.c_int32), c_int, c_int, c_int, c_float,
+                                                     vp, vp, c_int, ctypes.POINTER(vp)]
+    lib.varlen_causal_attn_runner_create.restype = c_int
+    lib.varlen_causal_attn_runner_run.argtypes = [vp, vp, i32p, c_int, c_int, c_int, vp, vp, ip]
+    lib.varlen_causal_attn_runner_run.restype = c_int
+    lib.varlen_causal_attn_runner_bucket.argtypes = [vp, c_int, c_int, ip]
+    lib.varlen_causal_attn_runner_bucket.restype = c_int
+    lib.varlen_causal_attn_runner_captured.argtypes = [vp, ip]
+    lib.varlen_causal_attn_runner_captured.restype = c_int
+    lib.varlen_causal_attn_runner_destroy.argtypes = [vp]
+    lib.varlen_causal_attn_runner_destroy.restype = c_int
     lib.varlen_causal_attn_tile_rows.argtypes = []
     lib.varlen_causal_attn_tile_rows.restype = c_int
     lib.varlen_causal_attn_strerror.argtypes = [c_int]
@@ -255,3 +273,87 @@ def fwd_with_worklist(qkv, cu_seqlens, max_seqlen: int, items, count, n_heads: i
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd_worklist")
     return out
+
+
+# The pages' token buckets: ten buckets from 2560 to 7168 in steps of 512
+# (cti2026 README, CUDA Graph section, bucketed padding).
+PAGES_BUCKETS = tuple(range(2560, 7168 + 1, 512))
+
+
+class GraphRunner:
+    """Bucketed graph runner over ``varlen_causal_attn_runner_*`` (argument marshalling only).
+
+    ``qkv_static`` / ``out_static`` are allocated here with torch (top-bucket rows)
+    and handed to the library, which captures one HIP graph per bucket over them.
+    ``run`` replays the bucket of a batch (or runs the eager forward above the top
+    bucket) and returns ``(out, bucket)``; with ``qkv`` the static buffer itself
+    (filled by the caller, e.g. ``runner.qkv_static[:T] = ...``) nothing is copied in.
+    """
+
+    def __init__(self, buckets=PAGES_BUCKETS, max_users: int = 20, n_heads: int = 8, head_dim: int = 64,
+                 scale: Optional[float] = None, precapture: bool = True, device="cuda"):
+        torch = _torch_mod()
+        self.buckets = tuple(int(b) for b in buckets)
+        self.max_users, self.n_heads, self.head_dim = int(max_users), int(n_heads), int(head_dim)
+        if head_dim != 64:
+            raise ValueError("head_dim must be 64")
+        self.scale = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+        top = max(self.buckets) if self.buckets else 0
+        self.qkv_static = torch.zeros((top, 3 * n_heads * head_dim), dtype=torch.bfloat16, device=device)
+        self.out_static = torch.zeros((top, n_heads * head_dim), dtype=torch.bfloat16, device=device)
+        self._handle = ctypes.c_void_p(None)
+        arr = (ctypes.c_int32 * max(1, len(self.buckets)))(*self.buckets)
+        with torch.cuda.device(self.qkv_static.device):
+            rc = library().varlen_causal_attn_runner_create(arr, len(self.buckets), self.max_users, self.n_heads,
+                                                            self.scale, self.qkv_static.data_ptr(),
+                                                            self.out_static.data_ptr(), 1 if precapture else 0,
+                                                            ctypes.byref(self._handle))
+        if rc != 0:
+            raise VlcaError(rc, "varlen_causal_attn_runner_create")
+
+    def bucket(self, num_users: int, total_tokens: int) -> int:
+        b = ctypes.c_int(-1)
+        rc = library().varlen_causal_attn_runner_bucket(self._handle, int(num_users), int(total_tokens),
+                                                        ctypes.byref(b))
+        if rc != 0:
+            raise VlcaError(rc, "varlen_causal_attn_runner_bucket")
+        return b.value
+
+    def captured(self) -> int:
+        n = ctypes.c_int(0)
+        rc = library().varlen_causal_attn_runner_captured(self._handle, ctypes.byref(n))
+        if rc != 0:
+            raise VlcaError(rc, "varlen_causal_attn_runner_captured")
+        return n.value
+
+    def run(self, qkv, cu_seqlens, total_tokens: int, max_seqlen: int, out=None):
+        """One batch; ``total_tokens`` = cu_seqlens[-1] as a host int (picks the bucket)."""
+        torch = _torch_mod()
+        _check_qkv(qkv, self.n_heads, self.head_dim)
+        if qkv.data_ptr() != self.qkv_static.data_ptr() and qkv.shape[0] != total_tokens:
+            raise ValueError("qkv must have total_tokens rows (or be the runner's static buffer)")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1 \
+                or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
+        if out is None:
+            out = torch.empty((total_tokens, self.n_heads * self.head_dim), dtype=torch.bfloat16, device=qkv.device)
+        b = ctypes.c_int(-1)
+        rc = library().varlen_causal_attn_runner_run(self._handle, qkv.data_ptr(), cu_seqlens.data_ptr(),
+                                                     cu_seqlens.shape[0] - 1, int(total_tokens), int(max_seqlen),
+                                                     out.data_ptr(), _stream_handle(qkv.device), ctypes.byref(b))
+        if rc != 0:
+            raise VlcaError(rc, "varlen_causal_attn_runner_run")
+        return out, b.value
+
+    def close(self):
+        if self._handle:
+            rc = library().varlen_causal_attn_runner_destroy(self._handle)
+            self._handle = ctypes.c_void_p(None)
+            if rc != 0:
+                raise VlcaError(rc, "varlen_causal_attn_runner_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass

@@ -398,6 +398,7 @@ const char* varlen_causal_attn_strerror(int code) {
     case VLCA_ERR_WORKSPACE: return "library workspace could not be allocated (or must grow during stream capture)";
     case VLCA_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case VLCA_ERR_SCRATCH: return "batch needs more worklist items than the no-allocation scratch holds";
+    case VLCA_ERR_BUCKETS: return "bucket sizes must be positive and strictly increasing (at most 64 buckets)";
     default: return "unknown error code";
   }
 }

@@ -77,6 +77,11 @@ inline bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, in
   return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
 
+// Fixed-length offsets for a captured graph: out[i] = min(cu_seqlens[min(i,
+// num_users)], total) for i = 0 .. max_users (num_users <= max_users).
+hipError_t launch_pad_offsets(const int32_t* cu_seqlens, int num_users, int total, int32_t* out, int max_users,
+                              hipStream_t stream);
+
 // Scratch memory of the no-allocation entry point: one fixed array per device
 // (file-scope in vlca_noalloc.hip), laid out as the split pool, its arrival
 // counters, then a worklist of kNoAllocItems items followed by its count and

@@ -1091,7 +1091,24 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(VLCA_ATTENTION_
 #undef VLCA_ATTENTION_ARGS
 #undef VLCA_ATTENTION_PARAMS
 
+// Offsets padded to a fixed user count: out[i] = min(cu[min(i, U)], total) for
+// i = 0 .. U_max, so users U .. U_max-1 have no rows and no offset passes total.
+__global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ cu, int U, int total,
+                                                          int32_t* __restrict__ out, int U_max) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i > U_max) return;
+  const int v = U > 0 ? cu[i < U ? i : U] : 0;
+  out[i] = v < 0 ? 0 : (v > total ? total : v);
+}
+
 }  // namespace
+
+hipError_t launch_pad_offsets(const int32_t* cu_seqlens, int num_users, int total, int32_t* out, int max_users,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3((max_users + 1 + 255) / 256), dim3(256), 0, stream, cu_seqlens,
+                     num_users, total, out, max_users);
+  return hipGetLastError();
+}
 
 hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_tiles, int4* items, int32_t* count,
                            int32_t* queue, const SplitArgs& split, hipStream_t stream) {
