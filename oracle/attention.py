@@ -70,6 +70,69 @@ def varlen_causal_attention(qkv: np.ndarray, cu_seqlens, n_heads: int, head_dim:
     return out
 
 
+def varlen_causal_attention_backward(qkv: np.ndarray, cu_seqlens, dout: np.ndarray, n_heads: int, head_dim: int,
+                                     scale: float) -> np.ndarray:
+    """fp64 gradient ``dL/dqkv`` ``[T, 3*n_heads*head_dim]`` of the forward above, given ``dout = dL/dout``.
+
+    The training step of the same op: the recsys README (github.com/cry-daniel/
+    recsys), FusedHSTULayer section, runs an attention backward
+    (``hstu_attn_varlen_bwd``) between the layer's other backward kernels; the
+    pages give no formula for it, so this is the derivative of the definition
+    written out.  Per user and head, with S = scale Q K^T (causal), P = rowwise
+    softmax(S), O = P V:
+      dV = P^T dO;   dP = dO V^T;   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik);
+      dQ = scale dS K;   dK = scale dS^T Q.
+    (sum_k P_ik dP_ik = dO_i . O_i.)  Columns of ``dqkv`` follow the qkv layout.
+    """
+    qkv = np.asarray(qkv, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    hd = n_heads * head_dim
+    T = int(cu[-1])
+    if qkv.shape != (T, 3 * hd) or dout.shape != (T, hd):
+        raise ValueError("shape mismatch")
+    dqkv = np.zeros_like(qkv)
+    for u in range(cu.shape[0] - 1):
+        s, e = int(cu[u]), int(cu[u + 1])
+        L = e - s
+        if L <= 0:
+            continue
+        allowed = np.tril(np.ones((L, L), dtype=bool))
+        for h in range(n_heads):
+            q, k, v = split_qkv_head(qkv, slice(s, e), h, n_heads, head_dim)
+            c = h * head_dim
+            do = dout[s:e, c:c + head_dim]
+            p = _masked_softmax_rows(scale * (q @ k.T), allowed)
+            dp = do @ v.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dqkv[s:e, c:c + head_dim] = scale * (ds @ k)
+            dqkv[s:e, hd + c:hd + c + head_dim] = scale * (ds.T @ q)
+            dqkv[s:e, 2 * hd + c:2 * hd + c + head_dim] = p.T @ do
+    return dqkv
+
+
+def varlen_causal_attention_lse(qkv: np.ndarray, cu_seqlens, n_heads: int, head_dim: int,
+                                scale: float) -> np.ndarray:
+    """fp64 ``[T, n_heads]``: ln sum_{j <= i} exp(scale q_i . k_j) over the row's user (the
+    softmax's normaliser in log form, which the backward uses to recompute P)."""
+    qkv = np.asarray(qkv, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    lse = np.zeros((T, n_heads), dtype=np.float64)
+    for u in range(cu.shape[0] - 1):
+        s, e = int(cu[u]), int(cu[u + 1])
+        L = e - s
+        if L <= 0:
+            continue
+        allowed = np.tril(np.ones((L, L), dtype=bool))
+        for h in range(n_heads):
+            q, k, _ = split_qkv_head(qkv, slice(s, e), h, n_heads, head_dim)
+            z = np.where(allowed, scale * (q @ k.T), -np.inf)
+            m = z.max(axis=1)
+            lse[s:e, h] = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return lse
+
+
 def varlen_causal_attention_rows(qkv: np.ndarray, cu_seqlens, rows, n_heads: int, head_dim: int,
                                  scale: float) -> np.ndarray:
     """fp64 output of the selected packed rows only, ``[len(rows), n_heads*head_dim]``.
