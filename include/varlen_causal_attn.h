@@ -124,6 +124,42 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
                            void* out, hipStream_t stream);
 
 /*
+ * Training forward: varlen_causal_attn_fwd (same plan, split decision and output
+ * bits) that also writes, for every row t of a user and head h,
+ *     lse[t*n_heads + h] = ln sum_{j <= i} exp(scale * q_i . k_j)
+ * (fp32 [T, n_heads], device, caller-owned; rows of no user are not written), the
+ * row log-sum-exp that varlen_causal_attn_bwd uses to recompute the softmax.
+ * Errors as for varlen_causal_attn_fwd; lse NULL with work to do is
+ * VLCA_ERR_NULL_POINTER.
+ */
+int varlen_causal_attn_fwd_lse(const void* qkv, const int32_t* cu_seqlens, int num_users,
+                               int max_seqlen, int n_heads, int head_dim, float scale,
+                               void* out, float* lse, hipStream_t stream);
+
+/*
+ * Backward pass: with L a loss and dout = dL/dout, writes dqkv = dL/dqkv, bf16
+ * [T, 3*n_heads*64] in the qkv layout (dq, dk, dv blocks; the training step of
+ * the same op: the recsys README, FusedHSTULayer backward, runs the attention
+ * backward between the layer's other backward kernels).  Per user and head, with
+ * P the forward's causal softmax recomputed from lse:
+ *     D = rowsum(dout o out),  dS = P o (dout V^T - D),
+ *     dV = P^T dout,  dK = scale dS^T Q,  dQ = scale dS K.
+ *   qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale: as given to
+ *          varlen_causal_attn_fwd_lse;
+ *   out    its bf16 output [T, n_heads*64];  lse: its fp32 [T, n_heads];
+ *   dout   bf16 [T, n_heads*64];
+ *   dqkv   bf16 [T, 3*n_heads*64], caller-owned, distinct from the inputs.  Every
+ *          row of a user is written; rows of no user are not touched.
+ * Deterministic (no atomics).  Uses the stream's worklist (as the forward's
+ * scheduler plan does: allocated or grown on first need, never freed).
+ * Asynchronous on `stream`; errors as for varlen_causal_attn_fwd, plus
+ * VLCA_ERR_ALIAS if dqkv is one of qkv, out, dout.
+ */
+int varlen_causal_attn_bwd(const void* qkv, const void* out, const void* dout, const float* lse,
+                           const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads,
+                           int head_dim, float scale, void* dqkv, hipStream_t stream);
+
+/*
  * For callers that cannot allocate (code under HIP graph capture, serving loops
  * that forbid hipMalloc): the same computation as varlen_causal_attn_fwd, with
  * the same launch plan and split decision and hence the same output bits, but

@@ -9,6 +9,8 @@ Contents:
   attention.varlen_causal_attention   per-user dense softmax(scale*QK^T + causal mask) V
   attention.varlen_causal_attention_rows  the same, one selected query row at a time
   attention.varlen_causal_attention_backward  dL/dqkv given dL/dout (derivative of the definition)
+  attention.varlen_causal_attention_backward_magnitude  each gradient element with every term
+                                      of its expansion taken in absolute value (for error bounds)
   attention.varlen_causal_attention_lse   each row's log-sum-exp of its scaled causal scores
   attention.dense_masked_attention    whole packed stream as one T x T problem with the
                                       block-diagonal causal mask built from the offsets
@@ -25,6 +27,7 @@ from .attention import (  # noqa: F401
     split_qkv_head,
     varlen_causal_attention,
     varlen_causal_attention_backward,
+    varlen_causal_attention_backward_magnitude,
     varlen_causal_attention_lse,
     varlen_causal_attention_rows,
 )

@@ -111,6 +111,43 @@ def varlen_causal_attention_backward(qkv: np.ndarray, cu_seqlens, dout: np.ndarr
     return dqkv
 
 
+def varlen_causal_attention_backward_magnitude(qkv: np.ndarray, cu_seqlens, dout: np.ndarray, n_heads: int,
+                                               head_dim: int, scale: float) -> np.ndarray:
+    """fp64 ``[T, 3*n_heads*head_dim]``: each gradient element of
+    ``varlen_causal_attention_backward`` evaluated with every term of its expansion
+    in the inputs and P replaced by its absolute value (sums of magnitudes, no
+    cancellation):
+      dS_mag_ij = P_ij (|dP|_ij + sum_d |dO_id| (P |V|)_id),  |dP| = |dO| |V|^T,
+      dQ_mag = scale dS_mag |K|,  dK_mag = scale dS_mag^T |Q|,  dV_mag = P^T |dO|.
+    Computing the gradient with each term perturbed by a relative error <= e
+    changes it by at most e times this (to first order), so a test's tolerance
+    for a rounded computation uses it; where terms cancel it far exceeds the
+    gradient.
+    """
+    qkv = np.asarray(qkv, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    hd = n_heads * head_dim
+    mag = np.zeros_like(qkv)
+    for u in range(cu.shape[0] - 1):
+        s, e = int(cu[u]), int(cu[u + 1])
+        L = e - s
+        if L <= 0:
+            continue
+        allowed = np.tril(np.ones((L, L), dtype=bool))
+        for h in range(n_heads):
+            q, k, v = split_qkv_head(qkv, slice(s, e), h, n_heads, head_dim)
+            c = h * head_dim
+            ado = np.abs(dout[s:e, c:c + head_dim])
+            p = _masked_softmax_rows(scale * (q @ k.T), allowed)
+            dmag = np.sum(ado * (p @ np.abs(v)), axis=1, keepdims=True)
+            dsmag = p * (ado @ np.abs(v).T + dmag)
+            mag[s:e, c:c + head_dim] = scale * (dsmag @ np.abs(k))
+            mag[s:e, hd + c:hd + c + head_dim] = scale * (dsmag.T @ np.abs(q))
+            mag[s:e, 2 * hd + c:2 * hd + c + head_dim] = p.T @ ado
+    return mag
+
+
 def varlen_causal_attention_lse(qkv: np.ndarray, cu_seqlens, n_heads: int, head_dim: int,
                                 scale: float) -> np.ndarray:
     """fp64 ``[T, n_heads]``: ln sum_{j <= i} exp(scale q_i . k_j) over the row's user (the

@@ -196,16 +196,25 @@ hipError_t launch_schedule(const int32_t*, int num_users, int max_tiles, int4* i
 }
 
 hipError_t launch_attention(const void*, const int4* items, const int32_t* count, int32_t*, int n_heads, float,
-                            const SplitArgs& split, void*, int grid, int layer_log2, hipStream_t stream) {
+                            const SplitArgs& split, void*, float*, int grid, int layer_log2, hipStream_t stream) {
   g.launches.push_back({'a', items, touch(items, count), 0, 0, n_heads, grid, layer_log2, split, stream});
   check_counters(split);
   return hipSuccess;
 }
 
 hipError_t launch_attention_fused(const void*, const int32_t*, int num_users, int max_tiles, int n_heads, float,
-                                  const SplitArgs& split, void*, int grid, int layer_log2, hipStream_t stream) {
+                                  const SplitArgs& split, void*, float*, int grid, int layer_log2,
+                                  hipStream_t stream) {
   g.launches.push_back({'f', nullptr, 0, num_users, max_tiles, n_heads, grid, layer_log2, split, stream});
   check_counters(split);
+  return hipSuccess;
+}
+
+hipError_t launch_backward(const void*, const void*, const void*, const float*, const int32_t*, int num_users,
+                           const int4* items, const int32_t* count, int64_t max_items, int n_heads, float,
+                           void*, int, hipStream_t stream) {
+  g.launches.push_back({'b', items, touch(items, count), num_users, (int)max_items, n_heads, 0, -1,
+                        {0, 0, 0, nullptr, nullptr}, stream});
   return hipSuccess;
 }
 

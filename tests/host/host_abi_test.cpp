@@ -238,6 +238,32 @@ static void test_graph_runner() {
   CHECK(varlen_causal_attn_runner_destroy(r) == VLCA_OK && varlen_causal_attn_runner_destroy(nullptr) == VLCA_OK);
 }
 
+static void test_training_entry_points() {
+  stub::reset();
+  static float lse_buf[16];
+  static char dout_buf[16], dqkv_buf[16];
+  const hipStream_t s = stream_id(11);
+  // fwd_lse: same plan as fwd; lse required.
+  CHECK(varlen_causal_attn_fwd_lse(QKV, CU, 60, 452, 8, 64, 0.125f, OUT, nullptr, s) == VLCA_ERR_NULL_POINTER);
+  CHECK(varlen_causal_attn_fwd_lse(QKV, CU, 60, 452, 8, 64, 0.125f, OUT, lse_buf, s) == VLCA_OK);
+  CHECK(g.launches.size() == 1 && g.launches[0].kind == 'f');
+  // bwd: argument checks, then the scheduler and the backward over the stream's worklist.
+  auto bwd = [&](const void* out, const void* dout, const float* lse, void* dqkv, int users, int ms) {
+    return varlen_causal_attn_bwd(QKV, out, dout, lse, CU, users, ms, 8, 64, 0.125f, dqkv, s);
+  };
+  CHECK(bwd(OUT, nullptr, lse_buf, dqkv_buf, 60, 452) == VLCA_ERR_NULL_POINTER);
+  CHECK(bwd(OUT, dout_buf, lse_buf, nullptr, 60, 452) == VLCA_ERR_NULL_POINTER);
+  CHECK(bwd(OUT, dout_buf, lse_buf, dout_buf, 60, 452) == VLCA_ERR_ALIAS);
+  CHECK(bwd(OUT, dout_buf, lse_buf, const_cast<void*>(QKV), 60, 452) == VLCA_ERR_ALIAS);
+  CHECK(bwd(OUT, dout_buf, lse_buf, dqkv_buf, 0, 452) == VLCA_OK && bwd(OUT, dout_buf, lse_buf, dqkv_buf, 60, 0) == VLCA_OK);
+  g.launches.clear();
+  CHECK(bwd(OUT, dout_buf, lse_buf, dqkv_buf, 60, 452) == VLCA_OK);
+  CHECK(g.launches.size() == 2 && g.launches[0].kind == 's' && g.launches[1].kind == 'b');
+  CHECK(g.launches[0].split.p <= 1 && g.launches[1].items == g.launches[0].items);
+  CHECK(g.launches[1].max_tiles == 60 * 8);  // the worklist bound passed to the kernels
+  CHECK(g.frees == 0 && g.syncs == 0);
+}
+
 int main() {
   setvbuf(stdout, nullptr, _IONBF, 0);
   test_argument_errors();
@@ -246,6 +272,7 @@ int main() {
   test_state_created_during_capture();
   test_noalloc_entry_point();
   test_graph_runner();
+  test_training_entry_points();
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
 }

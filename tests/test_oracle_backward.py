@@ -117,3 +117,35 @@ def test_lse_matches_logsumexp():
                 q = qkv[s + i, h * D:(h + 1) * D]
                 k = qkv[s:s + i + 1, H * D + h * D:H * D + (h + 1) * D]
                 assert abs(lse[s + i, h] - logsumexp(SCALE * (k @ q))) <= 1e-12
+
+
+def test_magnitude_bounds_the_gradient_and_is_tight_without_cancellation():
+    lengths = [5, 1, 30]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    qkv = _rand((36, 3 * H * D), 13)
+    dout = _rand((36, H * D), 14)
+    g = oracle.varlen_causal_attention_backward(qkv, cu, dout, H, D, SCALE)
+    m = oracle.varlen_causal_attention_backward_magnitude(qkv, cu, dout, H, D, SCALE)
+    assert np.all(m >= np.abs(g) - 1e-12)  # triangle inequality
+    assert np.max(m[:, :2 * H * D] - np.abs(g[:, :2 * H * D])) > 0.1  # dq, dk terms do cancel
+    # brute force on one dQ element: the expansion dQ_id = scale sum_j P_ij (dP_ij -
+    # sum_k P_ik dP_ik) k_jd with dP_ij = sum_e dO_ie v_je, every product in absolute value
+    s0, i, d = 6, 20, 3  # user 2 (rows 6..35), its row 20, dim 3, head 0
+    qq, kk, vv = (qkv[s0:s0 + 30, o:o + D] for o in (0, H * D, 2 * H * D))
+    z = SCALE * (kk[:i + 1] @ qq[i])
+    pr = np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+    do = dout[s0 + i, :D]
+    brute = 0.0
+    for j in range(i + 1):
+        a = sum(abs(do[e] * vv[j, e]) for e in range(D))
+        b = sum(pr[k2] * abs(do[e] * vv[k2, e]) for k2 in range(i + 1) for e in range(D))
+        brute += pr[j] * (a + b) * abs(kk[j, d])
+    assert abs(SCALE * brute - m[s0 + i, d]) <= 1e-10 * m[s0 + i, d]
+    # with dO >= 0 every dV term is >= 0: the bound is attained
+    pos = np.abs(dout)
+    g2 = oracle.varlen_causal_attention_backward(qkv, cu, pos, H, D, SCALE)
+    m2 = oracle.varlen_causal_attention_backward_magnitude(qkv, cu, pos, H, D, SCALE)
+    assert np.max(np.abs(m2[:, 2 * H * D:] - g2[:, 2 * H * D:])) <= 1e-12
+    # dV's bound is linear in |dO|
+    assert np.allclose(oracle.varlen_causal_attention_backward_magnitude(qkv, cu, 3 * dout, H, D, SCALE)[:, 2 * H * D:],
+                       3 * m[:, 2 * H * D:])

@@ -13,7 +13,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "VlcaError", "library", "library_path", "fwd", "fwd_noalloc", "build_worklist", "fwd_with_worklist",
+    "VlcaError", "library", "library_path", "fwd", "fwd_noalloc", "fwd_lse", "bwd", "attention",
+    "build_worklist", "fwd_with_worklist",
     "worklist_capacity", "single_kernel", "tile_rows", "strerror", "call_module", "EXPORTED_SYMBOLS",
     "GraphRunner", "PAGES_BUCKETS",
 ]
@@ -25,6 +26,8 @@ _call = None  # the CPython trampoline for fwd / fwd_worklist (ctypes when it is
 
 EXPORTED_SYMBOLS = (
     "varlen_causal_attn_fwd",
+    "varlen_causal_attn_fwd_lse",
+    "varlen_causal_attn_bwd",
     "varlen_causal_attn_fwd_noalloc",
     "varlen_causal_attn_worklist_capacity",
     "varlen_causal_attn_build_worklist",
@@ -62,6 +65,10 @@ def library():
     c_int, c_float = ctypes.c_int, ctypes.c_float
     lib.varlen_causal_attn_fwd.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
     lib.varlen_causal_attn_fwd.restype = c_int
+    lib.varlen_causal_attn_fwd_lse.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp, vp]
+    lib.varlen_causal_attn_fwd_lse.restype = c_int
+    lib.varlen_causal_attn_bwd.argtypes = [vp, vp, vp, vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
+    lib.varlen_causal_attn_bwd.restype = c_int
     lib.varlen_causal_attn_fwd_noalloc.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
     lib.varlen_causal_attn_fwd_noalloc.restype = c_int
     lib.varlen_causal_attn_worklist_capacity.argtypes = [c_int, c_int, i64p]
@@ -205,6 +212,93 @@ def fwd(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd")
     return out
+
+
+def fwd_lse(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
+            scale: Optional[float] = None, out=None, lse=None):
+    """:func:`fwd` that also returns the rows' log-sum-exp: ``(out, lse)``, lse fp32 [T, n_heads]."""
+    torch = _torch_mod()
+    _check_qkv(qkv, n_heads, head_dim)
+    cu = _check_cu(cu_seqlens)
+    out = _out_tensor(qkv, n_heads, head_dim, out)
+    if lse is None:
+        lse = torch.empty((qkv.shape[0], n_heads), dtype=torch.float32, device=qkv.device)
+    elif (tuple(lse.shape) != (qkv.shape[0], n_heads) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.get_device() != qkv.get_device()):
+        raise ValueError("lse must be a contiguous float32 [T, n_heads] tensor on the qkv device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    rc = library().varlen_causal_attn_fwd_lse(qkv.data_ptr(), cu.data_ptr(), cu.shape[0] - 1, int(max_seqlen),
+                                              int(n_heads), int(head_dim), float(scale), out.data_ptr(),
+                                              lse.data_ptr(), _stream_handle(qkv.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_fwd_lse")
+    return out, lse
+
+
+def bwd(qkv, out, dout, lse, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
+        scale: Optional[float] = None, dqkv=None):
+    """Gradient of the forward w.r.t. qkv given ``dout``; returns dqkv bf16 [T, 3*n_heads*head_dim]."""
+    torch = _torch_mod()
+    _check_qkv(qkv, n_heads, head_dim)
+    cu = _check_cu(cu_seqlens)
+    shape_o = (qkv.shape[0], n_heads * head_dim)
+    for name, t in (("out", out), ("dout", dout)):
+        if (tuple(t.shape) != shape_o or t.dtype != torch.bfloat16 or not t.is_contiguous()
+                or t.get_device() != qkv.get_device()):
+            raise ValueError(f"{name} must be a contiguous bfloat16 {shape_o} tensor on the qkv device")
+    if (tuple(lse.shape) != (qkv.shape[0], n_heads) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.get_device() != qkv.get_device()):
+        raise ValueError("lse must be a contiguous float32 [T, n_heads] tensor on the qkv device")
+    if dqkv is None:
+        dqkv = torch.empty_like(qkv)
+    elif (dqkv.shape != qkv.shape or dqkv.dtype != torch.bfloat16 or not dqkv.is_contiguous()
+          or dqkv.get_device() != qkv.get_device()):
+        raise ValueError("dqkv must be a contiguous bfloat16 tensor shaped like qkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    rc = library().varlen_causal_attn_bwd(qkv.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                          cu.data_ptr(), cu.shape[0] - 1, int(max_seqlen), int(n_heads),
+                                          int(head_dim), float(scale), dqkv.data_ptr(), _stream_handle(qkv.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_bwd")
+    return dqkv
+
+
+_autograd_fn = None
+
+
+def _attention_function():
+    """A torch.autograd.Function whose forward and backward are the two library calls."""
+    global _autograd_fn
+    if _autograd_fn is None:
+        torch = _torch_mod()
+
+        class VarlenCausalAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, qkv, cu_seqlens, max_seqlen, n_heads, head_dim, scale):
+                out, lse = fwd_lse(qkv, cu_seqlens, max_seqlen, n_heads, head_dim, scale)
+                ctx.save_for_backward(qkv, cu_seqlens, out, lse)
+                ctx.args = (max_seqlen, n_heads, head_dim, scale)
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                qkv, cu, out, lse = ctx.saved_tensors
+                max_seqlen, n_heads, head_dim, scale = ctx.args
+                dqkv = bwd(qkv, out, dout.contiguous(), lse, cu, max_seqlen, n_heads, head_dim, scale)
+                return dqkv, None, None, None, None, None
+
+        _autograd_fn = VarlenCausalAttention
+    return _autograd_fn
+
+
+def attention(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
+              scale: Optional[float] = None):
+    """Differentiable forward (autograd runs :func:`bwd`); same output as :func:`fwd`."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return _attention_function().apply(qkv, cu_seqlens, int(max_seqlen), int(n_heads), int(head_dim), float(scale))
 
 
 def fwd_noalloc(qkv, cu_seqlens, max_seqlen: int, out, n_heads: int = 8, head_dim: int = 64,

@@ -231,7 +231,7 @@ int get_split_pool(int dev, hipStream_t stream, StreamState* out) {
 // worklist (fixed assignment).  split: key-range splitting (fwd's scheduler plan
 // only; a caller's worklist always holds whole items).
 int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, float scale,
-                int4* items, int32_t* count, int32_t* queue, const vlca::SplitArgs& split, void* out,
+                int4* items, int32_t* count, int32_t* queue, const vlca::SplitArgs& split, void* out, float* lse,
                 hipStream_t stream, bool schedule) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
@@ -245,18 +245,15 @@ int launch_pair(const void* qkv, const int32_t* cu_seqlens, int num_users, int m
   const int grid = grid_size(dev, pairs, false);
   const int layer_log2 =
       queue ? -1 : snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
-  if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, split, out, grid, layer_log2,
+  if (vlca::launch_attention(qkv, items, count, queue, n_heads, scale * kLog2e, split, out, lse, grid, layer_log2,
                              stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads,
-                           int head_dim, float scale, void* out, hipStream_t stream) {
+// The forward pass; lse: null, or [T, n_heads] fp32 log-sum-exp output.
+int fwd_impl(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, int head_dim,
+             float scale, void* out, float* lse, hipStream_t stream) {
   int rc = check_attention_args(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out);
   if (rc != VLCA_OK) return rc;
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
@@ -283,7 +280,7 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
     if (split.p > 1) grid = grid_size(dev, pairs * kSplitParts, true);
     const int layer_log2 = snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
     if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, split, out,
-                                     grid, layer_log2, stream) != hipSuccess)
+                                     lse, grid, layer_log2, stream) != hipSuccess)
       return VLCA_ERR_HIP;
     return VLCA_OK;
   }
@@ -293,7 +290,45 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
   rc = get_workspace(dev, stream, split.p > 1 ? std::max<int64_t>(need, upr) : need, &st);
   if (rc != VLCA_OK) return rc;
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, st.items, workspace_count(&st),
-                     workspace_count(&st) + vlca::kQueueStride, split, out, stream, true);
+                     workspace_count(&st) + vlca::kQueueStride, split, out, lse, stream, true);
+}
+
+}  // namespace
+
+extern "C" {
+
+int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads,
+                           int head_dim, float scale, void* out, hipStream_t stream) {
+  return fwd_impl(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out, nullptr, stream);
+}
+
+int varlen_causal_attn_fwd_lse(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
+                               int n_heads, int head_dim, float scale, void* out, float* lse, hipStream_t stream) {
+  if (num_users > 0 && max_seqlen > 0 && lse == nullptr) return VLCA_ERR_NULL_POINTER;
+  return fwd_impl(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out, lse, stream);
+}
+int varlen_causal_attn_bwd(const void* qkv, const void* out, const void* dout, const float* lse,
+                           const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, int head_dim,
+                           float scale, void* dqkv, hipStream_t stream) {
+  int rc = check_attention_args(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out);
+  if (rc != VLCA_OK) return rc;
+  if (num_users > 0 && (dout == nullptr || lse == nullptr || dqkv == nullptr)) return VLCA_ERR_NULL_POINTER;
+  if (dqkv != nullptr && (dqkv == qkv || dqkv == out || dqkv == dout)) return VLCA_ERR_ALIAS;
+  if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  const int64_t need = required_capacity(num_users, max_seqlen);
+  StreamState st;
+  rc = get_workspace(dev, stream, need, &st);
+  if (rc != VLCA_OK) return rc;
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, st.items, workspace_count(&st), nullptr,
+                            vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
+    return VLCA_ERR_HIP;
+  if (vlca::launch_backward(qkv, out, dout, lse, cu_seqlens, num_users, st.items, workspace_count(&st), need, n_heads,
+                            scale, dqkv, cu_count(dev), stream) != hipSuccess)
+    return VLCA_ERR_HIP;
+  return VLCA_OK;
 }
 
 int varlen_causal_attn_fwd_noalloc(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
@@ -323,14 +358,14 @@ int varlen_causal_attn_fwd_noalloc(const void* qkv, const int32_t* cu_seqlens, i
     if (split.p > 1) grid = grid_size(dev, pairs * kSplitParts, true);
     const int layer_log2 = snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
     if (vlca::launch_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e, split, out,
-                                     grid, layer_log2, stream) != hipSuccess)
+                                     nullptr, grid, layer_log2, stream) != hipSuccess)
       return VLCA_ERR_HIP;
     return VLCA_OK;
   }
   int4* items = reinterpret_cast<int4*>(base + vlca::kNoAllocItemsOffset);
   int32_t* count = reinterpret_cast<int32_t*>(items + vlca::kNoAllocItems);
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale, items, count,
-                     count + vlca::kQueueStride, split, out, stream, true);
+                     count + vlca::kQueueStride, split, out, nullptr, stream, true);
 }
 
 int varlen_causal_attn_worklist_capacity(int num_users, int max_seqlen, int64_t* capacity) {
@@ -366,7 +401,7 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale,
                      reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), nullptr,
-                     vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, out, stream, false);
+                     vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, out, nullptr, stream, false);
 }
 
 int varlen_causal_attn_single_kernel(int num_users, int max_seqlen, int n_heads, int* single_kernel) {

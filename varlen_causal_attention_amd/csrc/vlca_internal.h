@@ -51,16 +51,18 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 // the work is known to fit in one round of the fixed assignment) log2 of the
 // slots between workgroups that share a CU, so that the assignment balances each
 // CU's items.
+// lse: null, or [T, n_heads] fp32 receiving each row's log-sum-exp of its scaled
+// scores (natural log).
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue, int n_heads,
-                            float scale_log2e, const SplitArgs& split, void* out, int grid, int layer_log2,
+                            float scale_log2e, const SplitArgs& split, void* out, float* lse, int grid, int layer_log2,
                             hipStream_t stream);
 
 // Attention alone with the ordering done inside the kernel (no worklist buffer):
 // for batches where fused_fits() holds.  split.p == 2 splits long items (needs
 // split.pool / split.ctr).
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
-                                  int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
-                                  int layer_log2, hipStream_t stream);
+                                  int n_heads, float scale_log2e, const SplitArgs& split, void* out, float* lse,
+                                  int grid, int layer_log2, hipStream_t stream);
 
 // Users the single-kernel plan takes at most (one per thread of a workgroup),
 // and the rounds of whole items a workgroup can run when it orders the work
@@ -76,6 +78,13 @@ inline bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, in
   // rounds = ceil(items * H / grid) when the grid is a multiple of H; items <= users x max q-tiles
   return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
+
+// Backward pass over the scheduler's worklist (whole items) of this batch:
+// D = rowsum(dO o O) into dqkv's dq columns, then the dK/dV kernel and the dQ
+// kernel (see vlca_backward.hip).  cus: compute units of the device.
+hipError_t launch_backward(const void* qkv, const void* out, const void* dout, const float* lse,
+                           const int32_t* cu_seqlens, int num_users, const int4* items, const int32_t* count,
+                           int64_t max_items, int n_heads, float scale, void* dqkv, int cus, hipStream_t stream);
 
 // Fixed-length offsets for a captured graph: out[i] = min(cu_seqlens[min(i,
 // num_users)], total) for i = 0 .. max_users (num_users <= max_users).

@@ -489,11 +489,12 @@ __device__ __forceinline__ void merge_parts(const float* other, int part, const 
 // units in the same order from cu_seqlens (only for batches with at most
 // kFusedUsers users and kFusedRounds rounds of whole items) and keeps their
 // descriptors; with sp.p > 1 the long items run as key-range parts.
-template <bool kFused, bool kSplit>
+template <bool kFused, bool kSplit, bool kLse>
 __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv, const int4* __restrict__ items,
                                                const int32_t* __restrict__ count, int32_t* __restrict__ queue,
                                                const int32_t* __restrict__ cu, int U, int max_tiles, int n_heads,
-                                               int layer_log2, float sl2, SplitArgs sp, uint16_t* __restrict__ out) {
+                                               int layer_log2, float sl2, SplitArgs sp, uint16_t* __restrict__ out,
+                                               float* __restrict__ lse) {
   // Two ring stages (K tile then V tile); tile j of an item lives in stage j%2.
   // The key loop is unrolled by two so that every LDS address is a per-lane
   // register plus an immediate.
@@ -911,6 +912,10 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       const int lq = lane & 15, g = lane >> 4;
       LDS char* const rows = st0 + 2048 * L.wid;
       const float inv = 1.0f / A.l[0];
+      // Log-sum-exp of the row's scaled scores (natural log), for the backward pass:
+      // sum_j exp(scale q.k_j) = 2^(m sl2) * l.
+      if (kLse && g == 0 && L.qr < len - q0)
+        lse[((int64_t)start + q0 + L.qr) * n_heads + h] = (A.m * sl2 + __builtin_amdgcn_logf(A.l[0])) * 0.6931471805599453f;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {  // dims 16d + 4g .. +3 of row lq: bytes 32d + 8g
         const u32x2 wv = {pack_bf16x2(A.o[d][0] * inv, A.o[d][1] * inv),
@@ -935,16 +940,18 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
 #define VLCA_ATTENTION_PARAMS                                                                                   \
   const uint16_t *__restrict__ qkv, const int4 *__restrict__ items, const int32_t *__restrict__ count,          \
       int32_t *__restrict__ queue, const int32_t *__restrict__ cu, int U, int max_tiles, int n_heads,             \
-      int layer_log2, float sl2, SplitArgs sp, uint16_t *__restrict__ out
-#define VLCA_ATTENTION_ARGS qkv, items, count, queue, cu, U, max_tiles, n_heads, layer_log2, sl2, sp, out
+      int layer_log2, float sl2, SplitArgs sp, uint16_t *__restrict__ out, float *__restrict__ lse
+#define VLCA_ATTENTION_ARGS qkv, items, count, queue, cu, U, max_tiles, n_heads, layer_log2, sl2, sp, out, lse
 
 // Four workgroups per CU (at most 128 VGPRs a lane) is the occupancy the tile
 // step is tuned for.  Every instance fits it without an occupancy bound; such a
 // bound made the compiler schedule the tile step worse (the 25523-token batch 8%
 // slower over a worklist).
-template <bool kFused, bool kSplit>
+// kLse: also write each row's log-sum-exp (the training forward); a template
+// flag, so that the plain forward's instances keep their registers.
+template <bool kFused, bool kSplit, bool kLse>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(VLCA_ATTENTION_PARAMS) {
-  attention_body<kFused, kSplit>(VLCA_ATTENTION_ARGS);
+  attention_body<kFused, kSplit, kLse>(VLCA_ATTENTION_ARGS);
 }
 
 #undef VLCA_ATTENTION_ARGS
@@ -977,33 +984,33 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 }
 
 hipError_t launch_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue, int n_heads,
-                            float scale_log2e, const SplitArgs& split, void* out, int grid, int layer_log2,
+                            float scale_log2e, const SplitArgs& split, void* out, float* lse, int grid, int layer_log2,
                             hipStream_t stream) {
-  if (split.p > 1)
-    hipLaunchKernelGGL((attention_kernel<false, true>), dim3(grid), dim3(kAttnThreads), 0, stream,
-                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, layer_log2,
-                       scale_log2e, split, static_cast<uint16_t*>(out));
-  else
-    hipLaunchKernelGGL((attention_kernel<false, false>), dim3(grid), dim3(kAttnThreads), 0, stream,
-                       static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, n_heads, layer_log2,
-                       scale_log2e, split, static_cast<uint16_t*>(out));
+  // The split-capable instance runs whole items as well (every unit of a list
+  // without split items is kind 0), so the training forward needs only that one.
+  auto* k = lse != nullptr     ? attention_kernel<false, true, true>
+            : split.p > 1      ? attention_kernel<false, true, false>
+                               : attention_kernel<false, false, false>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(qkv), items, count,
+                     queue, nullptr, 0, 0, n_heads, layer_log2, scale_log2e, split, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
-                                  int n_heads, float scale_log2e, const SplitArgs& split, void* out, int grid,
-                                  int layer_log2, hipStream_t stream) {
-  hipLaunchKernelGGL((attention_kernel<true, true>), dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), nullptr, nullptr, nullptr, cu_seqlens, num_users, max_tiles,
-                     n_heads, layer_log2, scale_log2e, split, static_cast<uint16_t*>(out));
+                                  int n_heads, float scale_log2e, const SplitArgs& split, void* out, float* lse,
+                                  int grid, int layer_log2, hipStream_t stream) {
+  auto* k = lse != nullptr ? attention_kernel<true, true, true> : attention_kernel<true, true, false>;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kAttnThreads), 0, stream, static_cast<const uint16_t*>(qkv), nullptr,
+                     nullptr, nullptr, cu_seqlens, num_users, max_tiles, n_heads, layer_log2, scale_log2e, split,
+                     static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 
 int attention_blocks_per_cu(bool fused) {
   int n = 0;
   const hipError_t e =
-      fused ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<true, true>, kAttnThreads, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<false, false>, kAttnThreads, 0);
+      fused ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<true, true, false>, kAttnThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<false, false, false>, kAttnThreads, 0);
   if (e != hipSuccess || n < 1) n = 1;
   return n;
 }

@@ -142,6 +142,14 @@ def draw_qkv(rng: np.random.Generator, total_tokens: int, cols: int = QKV_COLS, 
     return torch.from_numpy(x).to(torch.bfloat16)
 
 
+def draw_dout(total_tokens: int, n_heads: int = N_HEADS, seed: int = 1):
+    """An upstream gradient dL/dout for the backward: N(0,1) float32 draws of
+    ``[total_tokens, n_heads*64]`` rounded to bf16 (RNE), from its own seeded
+    generator, as a torch CPU tensor."""
+    rng = np.random.default_rng(seed)
+    return draw_qkv(rng, total_tokens, cols=n_heads * HEAD_DIM)
+
+
 def make_config(idx: int, seed: int = 0, with_values: bool = True) -> Workload:
     rng = np.random.default_rng(seed)
     lengths, max_seqlen, vscale = config_lengths(idx, rng)
