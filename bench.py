@@ -6,6 +6,7 @@ kernel) over the packed batch, with qkv and cu_seqlens already resident in HBM.
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py --mode bwd [--config 2]   # the training backward (varlen_causal_attn_bwd)
 
 The default workload is the pages' size: 6823 packed tokens over 60 users,
 8 heads x 64, bf16 qkv [6823, 1536] (synthetic, seeded; see workloads.py).
@@ -26,19 +27,29 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-KERNEL_SRC = os.path.join(ROOT, "varlen_causal_attention_amd", "csrc", "vlca_kernels.hip")
-ATTN_KERNEL = "attention_kernel"           # <true, true>: single-kernel plan; <false, ...>: over a worklist
+CSRC = os.path.join(ROOT, "varlen_causal_attention_amd", "csrc")
+# The device sources each measured path runs (the profiles record their hash).
+KERNEL_SOURCES = {
+    "fwd": ("vlca_device.h", "vlca_kernels.hip"),
+    "bwd": ("vlca_device.h", "vlca_kernels.hip", "vlca_backward.hip"),
+}
+ATTN_KERNEL = "attention_kernel"  # <true, true, false>: single-kernel plan; <false, ...>: over a worklist
+PROFILE_PREFIX = {"fwd": "attention_kernel", "bwd": "backward"}
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(mode: str = "fwd") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[mode]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"attention_kernel_{workload_name}_pmc.txt")
+def measured_traffic(workload_name: str, mode: str = "fwd"):
+    """HBM bytes per measured unit (the forward's attention kernel, or one backward
+    call) from the committed rocprofv3 PMC summary, if it was taken on the current
+    kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{PROFILE_PREFIX[mode]}_{workload_name}_pmc.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -47,7 +58,7 @@ def measured_traffic(workload_name: str):
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(mode):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -55,8 +66,9 @@ def measured_traffic(workload_name: str):
         return None
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle as it stands, timed on this host over whole passes of the workload."""
+def cpu_baseline(w, budget_s: float, dout=None):
+    """The fp64 oracle as it stands (the backward when ``dout`` is given), timed on
+    this host over whole passes of the workload."""
     import numpy as np
     import torch
 
@@ -68,10 +80,14 @@ def cpu_baseline(w, budget_s: float):
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = os.cpu_count() or 1
     q = w.qkv_bf16.to(torch.float64).numpy()
+    d = None if dout is None else dout.to(torch.float64).numpy()
     passes = 0
     t0 = time.perf_counter()
     while True:
-        oracle.varlen_causal_attention(q, w.cu_seqlens, w.n_heads, w.head_dim, w.scale)
+        if d is None:
+            oracle.varlen_causal_attention(q, w.cu_seqlens, w.n_heads, w.head_dim, w.scale)
+        else:
+            oracle.varlen_causal_attention_backward(q, w.cu_seqlens, d, w.n_heads, w.head_dim, w.scale)
         passes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -81,18 +97,25 @@ def cpu_baseline(w, budget_s: float):
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{passes} full pass(es) of the {w.name} batch ({w.total_tokens} tokens, {w.num_users} users), "
-                  f"fp64 numpy, {dt:.1f} s wall",
+        "sample": f"{passes} full pass(es) of the {'backward' if d is not None else 'forward'} over the {w.name} "
+                  f"batch ({w.total_tokens} tokens, {w.num_users} users), fp64 numpy, {dt:.1f} s wall",
     }
 
 
+# Counters of the SQ pass (eight SQ counters and one GRBM counter: within what
+# one rocprofv3 pass can collect).
+SQ_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32",
+               "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE")
+
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o run -- "
-             "python3 {r}/bench.py --config {c} --steps 200 --warmup 2000 --no-cpu-baseline --cold-steps 0",
+             "python3 {r}/bench.py --mode {m} --config {c} --steps 200 --warmup 2000 --no-cpu-baseline --cold-steps 0",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/fetch -o run -- "
-             "python3 {r}/bench.py --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
+             "python3 {r}/bench.py --mode {m} --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run -- "
-             "python3 {r}/bench.py --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
+             "python3 {r}/bench.py --mode {m} --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
+    "sq": "rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " --output-format csv -d {out}/sq -o run -- "
+          "python3 {r}/bench.py --mode {m} --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
     "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/copyf -o run -- "
              "python3 {r}/bench.py --calibrate-copy-mib 256 --steps 5",
     "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/copyw -o run -- "
@@ -117,38 +140,44 @@ def _counter_mean(d: str, kernel_substr: str, counter: str):
     return sum(vals) / len(vals), len(vals)
 
 
-def summarize_profiles(root: str, config: int) -> None:
-    """Write profiles/attention_kernel_<workload>_{trace,pmc}.txt from rocprofv3 CSV output.
+def _short_name(name: str) -> str:
+    m = re.search(r"([A-Za-z_]\w*(?:<[^>]*>)?)\(", name)
+    return m.group(1) if m else name[:40]
+
+
+def summarize_profiles(root: str, config: int, mode: str = "fwd") -> None:
+    """Write profiles/<prefix>_<workload>_{trace,pmc,sq}.txt from rocprofv3 CSV output.
 
     ``root`` holds one folder per rocprofv3 run (commands in PROFILE_COMMANDS, with
     $REPO the repository root and $OUT the directory given to the runs, here
-    ``root``; run from /tmp with TMPDIR=/tmp), plus
-    ``kernel_sha.txt`` (sha256 of the kernel source the runs used) and, optionally,
-    ``trace.log`` (that run's stdout/stderr with the bench line).
+    ``root``; run from /tmp with TMPDIR=/tmp), plus ``kernel_sha.txt`` (the
+    kernel_source_hash of the mode the runs used) and, optionally, ``trace.log``
+    (that run's output with the bench line).  prefix: attention_kernel (forward)
+    or backward.
     """
     import workloads
 
     w = workloads.make_config(config, with_values=False)
+    prefix = PROFILE_PREFIX[mode]
     sha_path = os.path.join(root, "kernel_sha.txt")
     sha = open(sha_path, encoding="utf-8").read().split()[0][:16] if os.path.exists(sha_path) else "unknown"
-    if sha != kernel_source_hash():
-        print(f"warning: profiles were taken on kernel source {sha}, tree has {kernel_source_hash()}",
+    if sha != kernel_source_hash(mode):
+        print(f"warning: profiles were taken on kernel sources {sha}, tree has {kernel_source_hash(mode)}",
               file=sys.stderr)
-    cmds = {k: "cd /tmp && export TMPDIR=/tmp && " + v.format(r="$REPO", out="$OUT", c=config)
+    cmds = {k: "cd /tmp && export TMPDIR=/tmp && " + v.format(r="$REPO", out="$OUT", c=config, m=mode)
             for k, v in PROFILE_COMMANDS.items()}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out_base = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}")
 
     # Kernel trace: per-kernel duration statistics.
     stats = _read_csv(os.path.join(root, "trace", "run_kernel_stats.csv"))
-    lines = [f"# rocprofv3 kernel trace, workload {w.name} ({w.total_tokens} tokens, {w.num_users} users)",
+    lines = [f"# rocprofv3 kernel trace, {mode} workload {w.name} ({w.total_tokens} tokens, {w.num_users} users)",
              f"# command: {cmds['trace']}",
              f"kernel_source_sha256_16: {sha}",
              "",
-             f"{'kernel':<28} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+             f"{'kernel':<40} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
     for r in stats:
-        m = re.search(r"([A-Za-z_]\w*(?:<[^>]*>)?)\(", r["Name"])
-        short = m.group(1) if m else r["Name"][:28]
-        lines.append(f"{short:<28} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.3f} "
+        lines.append(f"{_short_name(r['Name']):<40} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.3f} "
                      f"{float(r['MinNs']) / 1e3:>9.3f} {float(r['MaxNs']) / 1e3:>9.3f} "
                      f"{float(r['Percentage']):>6.2f}")
     log = os.path.join(root, "trace.log")
@@ -157,24 +186,37 @@ def summarize_profiles(root: str, config: int) -> None:
         if bench_lines:
             lines += ["", "# the profiled bench run printed (its event timings include profiler overhead):"]
             lines += ["#   " + ln.rstrip()[:400] for ln in bench_lines]
-    with open(os.path.join(ROOT, "profiles", f"attention_kernel_{w.name}_trace.txt"), "w", encoding="utf-8") as f:
+    with open(out_base + "_trace.txt", "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
 
-    # HBM traffic: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy's reading,
-    # for the attention kernel fwd runs (the single-kernel instance when present).
+    # HBM traffic: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy's
+    # reading.  Forward: the attention kernel that fwd runs.  Backward: the sum
+    # over the kernels of one varlen_causal_attn_bwd call.
     fetch_rows = _read_csv(os.path.join(root, "fetch", "run_counter_collection.csv"))
-    kern = f"{ATTN_KERNEL}<true, true>" if any(f"{ATTN_KERNEL}<true, true>" in r["Kernel_Name"] for r in fetch_rows) \
-        else f"{ATTN_KERNEL}<false"
-    fetch_kib, n_f = _counter_mean(os.path.join(root, "fetch"), kern, "FETCH_SIZE")
-    write_kib, n_w = _counter_mean(os.path.join(root, "write"), kern, "WRITE_SIZE")
     copy_f, _ = _counter_mean(os.path.join(root, "copyf"), COPY_KERNEL, "FETCH_SIZE")
     copy_w, _ = _counter_mean(os.path.join(root, "copyw"), COPY_KERNEL, "WRITE_SIZE")
     copy_bytes = 256 * 2**20
     f_factor = copy_bytes / (copy_f * 1024.0)
     w_factor = copy_bytes / (copy_w * 1024.0)
+    if mode == "fwd":
+        names = [n for n in (f"{ATTN_KERNEL}<true, true, false>", f"{ATTN_KERNEL}<false, true, false>",
+                             f"{ATTN_KERNEL}<false, false, false>") if any(n in r["Kernel_Name"] for r in fetch_rows)]
+        kernels = names[:1]
+        algorithmic = w.algorithmic_bytes()
+    else:
+        kernels = ["bwd_preprocess_kernel", "schedule_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+        algorithmic = backward_algorithmic_bytes(w)
+    fetch_kib = write_kib = 0.0
+    per = []
+    for k in kernels:
+        fk, n_f = _counter_mean(os.path.join(root, "fetch"), k, "FETCH_SIZE")
+        wk, n_w = _counter_mean(os.path.join(root, "write"), k, "WRITE_SIZE")
+        fetch_kib += fk
+        write_kib += wk
+        per.append(f"{k}: fetch_kib {fk:.3f} ({n_f} dispatches), write_kib {wk:.3f} ({n_w} dispatches)")
     rd = fetch_kib * 1024.0 * f_factor
     wr = write_kib * 1024.0 * w_factor
-    lines = [f"# rocprofv3 HBM counters for {kern}, workload {w.name}",
+    lines = [f"# rocprofv3 HBM counters, {mode} workload {w.name}",
              f"# command (fetch): {cmds['fetch']}",
              f"# command (write): {cmds['write']}",
              f"# command (copy calibration, fetch): {cmds['copyf']}",
@@ -183,11 +225,10 @@ def summarize_profiles(root: str, config: int) -> None:
              "# 256 MiB device-to-device copy (known bytes), averaged over the dispatches listed.",
              f"kernel_source_sha256_16: {sha}",
              f"workload: {w.name}",
-             f"kernel: {kern}",
+             f"kernels: {', '.join(kernels)}",
+             *[f"# {x}" for x in per],
              f"fetch_kib_per_dispatch: {fetch_kib:.3f}",
-             f"fetch_dispatches: {n_f}",
              f"write_kib_per_dispatch: {write_kib:.3f}",
-             f"write_dispatches: {n_w}",
              f"copy_bytes: {copy_bytes}",
              f"copy_fetch_kib: {copy_f:.3f}",
              f"copy_write_kib: {copy_w:.3f}",
@@ -196,25 +237,82 @@ def summarize_profiles(root: str, config: int) -> None:
              f"hbm_read_bytes_per_launch: {rd:.0f}",
              f"hbm_write_bytes_per_launch: {wr:.0f}",
              f"hbm_bytes_per_launch: {rd + wr:.0f}",
-             f"algorithmic_bytes_per_launch: {w.algorithmic_bytes()}",
-             f"traffic_over_algorithmic: {(rd + wr) / w.algorithmic_bytes():.4f}"]
-    with open(os.path.join(ROOT, "profiles", f"attention_kernel_{w.name}_pmc.txt"), "w", encoding="utf-8") as f:
+             f"algorithmic_bytes_per_launch: {algorithmic}",
+             f"traffic_over_algorithmic: {(rd + wr) / algorithmic:.4f}"]
+    with open(out_base + "_pmc.txt", "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+    # SQ counters per kernel (per dispatch, averaged) and what they give.
+    sq_dir = os.path.join(root, "sq")
+    if os.path.exists(os.path.join(sq_dir, "run_counter_collection.csv")):
+        rows = _read_csv(os.path.join(sq_dir, "run_counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            k = _short_name(r["Kernel_Name"])
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        simds = 4 * 256
+        lines = [f"# rocprofv3 SQ counters, {mode} workload {w.name}: per-dispatch averages",
+                 f"# command: {cmds['sq']}",
+                 "# SQ_* are summed over the device's shader engines and XCDs; GRBM_GUI_ACTIVE is summed",
+                 "# over the 8 XCDs, so GUI cycles of the dispatch = GRBM_GUI_ACTIVE / 8.",
+                 "# mfma_busy_pct = SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles x 1024 SIMDs) x 100",
+                 "# lds_bank_conflict_pct = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE x 100",
+                 f"kernel_source_sha256_16: {sha}"]
+        for k in sorted(acc):
+            c = {n: sum(v) / len(v) for n, v in acc[k].items()}
+            n = len(next(iter(acc[k].values())))
+            lines.append("")
+            lines.append(f"kernel: {k} ({n} dispatches)")
+            for name in SQ_COUNTERS:
+                if name in c:
+                    lines.append(f"  {name}: {c[name]:.0f}")
+            gui = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+            mf = c.get("SQ_INSTS_MFMA", 0.0)
+            if gui > 0:
+                lines.append(f"  gui_cycles: {gui:.0f}")
+                lines.append(f"  mfma_busy_pct: {100.0 * c.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / (gui * simds):.2f}")
+            if mf > 0:
+                lines.append(f"  mfma_busy_cycles_per_mfma: {c.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / mf:.2f}")
+                lines.append(f"  valu_per_mfma: {c.get('SQ_INSTS_VALU', 0.0) / mf:.2f}")
+                lines.append(f"  trans_f32_per_mfma: {c.get('SQ_INSTS_VALU_TRANS_F32', 0.0) / mf:.3f}")
+                lines.append(f"  lds_insts_per_mfma: {c.get('SQ_INSTS_LDS', 0.0) / mf:.3f}")
+            if c.get("SQ_LDS_IDX_ACTIVE", 0.0) > 0:
+                lines.append(f"  lds_bank_conflict_pct: "
+                             f"{100.0 * c.get('SQ_LDS_BANK_CONFLICT', 0.0) / c['SQ_LDS_IDX_ACTIVE']:.3f}")
+        with open(out_base + "_sq.txt", "w", encoding="utf-8") as f:
+            f.write("\n".join(lines) + "\n")
+
+
+def backward_algorithmic_bytes(w) -> int:
+    """qkv, out and dout read once, lse read once, dqkv written once."""
+    hd = w.n_heads * w.head_dim
+    return w.total_tokens * ((3 + 1 + 1 + 3) * hd * 2 + w.n_heads * 4)
 
 
 # The pages' own figure for this path: their Triton varlen kernel took 0.111 ms on
 # the 6,823-token / 60-user batch (cti2026 README page, FlashAttention_Varlen
-# section; the hardware is not stated beside it).  It is context, not a target:
-# vs_baseline is the ratio of this build's tokens/s to that figure's, on that
-# batch only.
+# section; the hardware is not stated beside it, the deployment targets another
+# GPU).  Another machine's number is context, not a baseline: vs_baseline is
+# null and the ratio is reported as pages_ratio, on that batch only.
 PAGES_6823_MS = 0.111
 
 
-def vs_baseline(w, tokens_per_s):
+def pages_ratio(w, tokens_per_s):
     if w.total_tokens != 6823 or w.num_users != 60:
         return None
     return tokens_per_s / (w.total_tokens / (PAGES_6823_MS * 1e-3))
+
+
+def roofline(flops: float, nbytes: float, seconds: float, traffic, kernel: str, **extra):
+    """The roofline object: HBM-bound below the ridge (GB/s vs 8 TB/s), MFMA-bound above it."""
+    if flops / nbytes < RIDGE:
+        bound, achieved, peak, unit = "hbm", nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / seconds / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": traffic, "kernel": kernel, "kernel_us": seconds * 1e6, "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops, **extra}
 
 
 def main():
@@ -226,6 +324,8 @@ def main():
     # batch read 48.4 us, with 2000 42.7 us).
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = 6823 tokens / 60 users)")
+    ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: the forward (the default measurement); bwd: the training backward")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -238,7 +338,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles, args.config)
+        summarize_profiles(args.summarize_profiles, args.config, args.mode)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -267,6 +367,9 @@ def main():
                           "launches": args.steps}), flush=True)
         return
     w = workloads.make_config(args.config)
+    if args.mode == "bwd":
+        run_backward(args, w, dev)
+        return
     qkv = w.qkv_bf16.to(dev)
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     out = torch.empty((w.total_tokens, w.n_heads * w.head_dim), dtype=torch.bfloat16, device=dev)
@@ -308,7 +411,8 @@ def main():
     torch.cuda.synchronize()
     ms_worklist_kernel = e0.elapsed_time(e1) / args.steps
     ms_attn = ms_step if single else ms_worklist_kernel
-    kernel_name = f"{ATTN_KERNEL}<true, true>" if single else f"{ATTN_KERNEL}<false, ...>"
+    kernel_name = (f"{ATTN_KERNEL}<true, true, false>" if single
+                   else f"{ATTN_KERNEL}<false, false, false> over a prebuilt worklist (fixed assignment)")
     print(f"[bench] step {ms_step * 1e3:.2f} us ({'single kernel' if single else 'scheduler + attention'}), "
           f"attention kernel over a worklist {ms_worklist_kernel * 1e3:.2f} us", file=sys.stderr, flush=True)
 
@@ -331,11 +435,6 @@ def main():
     flops = w.causal_flops()
     nbytes = w.algorithmic_bytes()
     tflops = flops / (ms_step * 1e-3) / 1e12
-    ai = flops / nbytes
-    if ai < RIDGE:
-        bound, achieved, peak, unit = "hbm", nbytes / (ms_attn * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
-    else:
-        bound, achieved, peak, unit = "mfma", flops / (ms_attn * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     traffic = measured_traffic(w.name)
 
     value = w.total_tokens / (ms_step * 1e-3)
@@ -349,7 +448,8 @@ def main():
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": vs_baseline(w, value),
+        "vs_baseline": None,
+        "pages_ratio": pages_ratio(w, value),
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
@@ -367,22 +467,75 @@ def main():
         "tflops": tflops,
         "pct_bf16_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "causal_gflop": flops / 1e9,
-        "roofline": {
-            "bound": bound,
-            "achieved": achieved,
-            "peak": peak,
-            "unit": unit,
-            "frac": achieved / peak,
-            "traffic": traffic,
-            "kernel": kernel_name,
-            "kernel_us": ms_attn * 1e3,
-            "worklist_kernel_us": ms_worklist_kernel * 1e3,
-            "algorithmic_bytes": nbytes,
-            "algorithmic_flops": flops,
-        },
+        "roofline": roofline(flops, nbytes, ms_attn * 1e-3, traffic, kernel_name,
+                             worklist_kernel_us=ms_worklist_kernel * 1e3),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+def run_backward(args, w, dev):
+    """One step = one varlen_causal_attn_bwd call (D preprocess, scheduler, dK/dV and
+    dQ kernels) over the batch, with qkv, out, dout and lse resident in HBM."""
+    import torch
+
+    import varlen_causal_attention_amd as vlca
+    import workloads
+
+    qkv = w.qkv_bf16.to(dev)
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    dout_cpu = workloads.draw_dout(w.total_tokens, w.n_heads, seed=1)
+    dout = dout_cpu.to(dev)
+    out, lse = vlca.fwd_lse(qkv, cu, w.max_seqlen, n_heads=w.n_heads, scale=w.scale)
+    dqkv = torch.empty_like(qkv)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        vlca.bwd(qkv, out, dout, lse, cu, w.max_seqlen, n_heads=w.n_heads, scale=w.scale, dqkv=dqkv)
+
+    print(f"[bench] backward {w.name}: T={w.total_tokens} U={w.num_users} max_seqlen={w.max_seqlen} "
+          f"warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] backward step {ms_step * 1e3:.2f} us", file=sys.stderr, flush=True)
+    # Algorithmic work: the four products dV = P^T dO, dP = dO V^T, dQ = dS K and
+    # dK = dS^T Q over the causal triangle (twice the forward's two); bytes: qkv,
+    # out, dout and lse read once, dqkv written once.
+    flops = 2.0 * w.causal_flops()
+    nbytes = backward_algorithmic_bytes(w)
+    value = w.total_tokens / (ms_step * 1e-3)
+    rec = {
+        "metric": "varlen causal attn bwd tokens/s + TFLOP/s (% bf16 MFMA peak)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": w.total_tokens, "num_users": w.num_users,
+                   "max_seqlen": w.max_seqlen, "n_heads": w.n_heads, "head_dim": w.head_dim,
+                   "pass": "backward (dq, dk, dv from dout, out, lse)"},
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": roofline(flops, nbytes, ms_step * 1e-3, measured_traffic(w.name, "bwd"),
+                             "varlen_causal_attn_bwd (preprocess, scheduler, dK/dV and dQ kernels)"),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, dout=dout_cpu)
     print(json.dumps(rec), flush=True)
 
 
