@@ -12,6 +12,8 @@ Contents:
   attention.varlen_causal_attention_backward_magnitude  each gradient element with every term
                                       of its expansion taken in absolute value (for error bounds)
   attention.varlen_causal_attention_lse   each row's log-sum-exp of its scaled causal scores
+  attention.hstu_mask, varlen_attention_masked  the HSTU-style mask variants (context, candidate
+                                      groups, sliding / bidirectional window)
   attention.dense_masked_attention    whole packed stream as one T x T problem with the
                                       block-diagonal causal mask built from the offsets
   attention.block_diagonal_causal_mask
@@ -24,7 +26,9 @@ single-segment special case, hand-derived fixtures under ``tests/golden/``).
 from .attention import (  # noqa: F401
     block_diagonal_causal_mask,
     dense_masked_attention,
+    hstu_mask,
     split_qkv_head,
+    varlen_attention_masked,
     varlen_causal_attention,
     varlen_causal_attention_backward,
     varlen_causal_attention_backward_magnitude,

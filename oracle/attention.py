@@ -170,6 +170,60 @@ def varlen_causal_attention_lse(qkv: np.ndarray, cu_seqlens, n_heads: int, head_
     return lse
 
 
+def hstu_mask(L: int, c: int = 0, g: int = 0, group: int = 1, window=(-1, 0)) -> np.ndarray:
+    """Boolean ``[L, L]`` mask of one user (entry (i, j): query row i sees key j).
+
+    The recsys README (github.com/cry-daniel/recsys), HSTU section, gives the
+    sequence as [contextual tokens][historical tokens][candidate tokens] --
+    contextual tokens attended bidirectionally, history causally, candidates in
+    groups of target_group_size -- and ``window_size=(-1, 0)`` as the causal
+    default of its local mask.  Reading taken (the page gives only this layout):
+    with nc = L - g,
+      right == 0: every row sees the context keys j < c; a row i >= c sees the
+        history keys max(c, i - left) <= j <= min(i, nc - 1) (left -1: no bound);
+        a candidate row i >= nc also sees its own group's keys gs(i) <= j <= i,
+        gs(i) = nc + floor((i - nc) / group) * group;
+      otherwise (c = g = 0): i - left <= j <= i + right (-1: no bound that side).
+    """
+    left, right = window
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    lo = np.maximum(0, i - left) if left >= 0 else np.zeros_like(i)
+    if right != 0:
+        if c or g:
+            raise ValueError("contexts and targets need a causal window")
+        hi = np.minimum(L - 1, i + right) if right >= 0 else np.full_like(i, L - 1)
+        return (j >= lo) & (j <= hi)
+    nc = L - g
+    ctx = j < c
+    hist = (i >= c) & (j >= np.maximum(c, lo)) & (j <= np.minimum(i, nc - 1))
+    gs = nc + ((i - nc) // group) * group
+    grp = (i >= nc) & (j >= gs) & (j <= i)
+    return ctx | hist | grp
+
+
+def varlen_attention_masked(qkv: np.ndarray, cu_seqlens, n_heads: int, head_dim: int, scale: float,
+                            num_contexts=None, num_targets=None, group: int = 1, window=(-1, 0)) -> np.ndarray:
+    """fp64 ``[T, n_heads*head_dim]``: per user and head, softmax(scale Q K^T restricted to
+    ``hstu_mask``) V, the user's context / candidate counts clamped to its length."""
+    qkv = np.asarray(qkv, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    out = np.zeros((T, n_heads * head_dim), dtype=np.float64)
+    for u in range(cu.shape[0] - 1):
+        s, e = int(cu[u]), int(cu[u + 1])
+        L = e - s
+        if L <= 0:
+            continue
+        c = min(max(int(num_contexts[u]), 0), L) if num_contexts is not None else 0
+        g = min(max(int(num_targets[u]), 0), L - c) if num_targets is not None else 0
+        allowed = hstu_mask(L, c, g, group, window)
+        for h in range(n_heads):
+            q, k, v = split_qkv_head(qkv, slice(s, e), h, n_heads, head_dim)
+            out[s:e, h * head_dim:(h + 1) * head_dim] = _masked_softmax_rows(scale * (q @ k.T), allowed) @ v
+    return out
+
+
 def varlen_causal_attention_rows(qkv: np.ndarray, cu_seqlens, rows, n_heads: int, head_dim: int,
                                  scale: float) -> np.ndarray:
     """fp64 output of the selected packed rows only, ``[len(rows), n_heads*head_dim]``.
