@@ -32,9 +32,10 @@ CSRC = os.path.join(ROOT, "varlen_causal_attention_amd", "csrc")
 KERNEL_SOURCES = {
     "fwd": ("vlca_device.h", "vlca_kernels.hip"),
     "bwd": ("vlca_device.h", "vlca_kernels.hip", "vlca_backward.hip"),
+    "masked": ("vlca_device.h", "vlca_kernels.hip", "vlca_masked.hip"),
 }
 ATTN_KERNEL = "attention_kernel"  # <true, true, false>: single-kernel plan; <false, ...>: over a worklist
-PROFILE_PREFIX = {"fwd": "attention_kernel", "bwd": "backward"}
+PROFILE_PREFIX = {"fwd": "attention_kernel", "bwd": "backward", "masked": "masked_attention_kernel"}
 
 
 def kernel_source_hash(mode: str = "fwd") -> str:
@@ -324,8 +325,9 @@ def main():
     # batch read 48.4 us, with 2000 42.7 us).
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = 6823 tokens / 60 users)")
-    ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd",
-                    help="fwd: the forward (the default measurement); bwd: the training backward")
+    ap.add_argument("--mode", choices=("fwd", "bwd", "masked"), default="fwd",
+                    help="fwd: the forward (the default measurement); bwd: the training backward; "
+                         "masked: the forward with an HSTU-style mask (MASK_RECIPE)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -369,6 +371,9 @@ def main():
     w = workloads.make_config(args.config)
     if args.mode == "bwd":
         run_backward(args, w, dev)
+        return
+    if args.mode == "masked":
+        run_masked(args, w, dev)
         return
     qkv = w.qkv_bf16.to(dev)
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
@@ -473,6 +478,95 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)
+
+
+# The masked forward's workload: HSTU-like users with up to 16 context tokens and
+# up to 32 candidates in groups of 8, and a 256-token causal window (counts drawn
+# per user from their own seeded generator).
+MASK_RECIPE = {"contexts_max": 16, "targets_max": 32, "group": 8, "window": (256, 0), "seed": 7}
+
+
+def mask_counts(w):
+    import numpy as np
+
+    rng = np.random.default_rng(MASK_RECIPE["seed"])
+    c = rng.integers(0, MASK_RECIPE["contexts_max"] + 1, w.num_users)
+    g = rng.integers(0, MASK_RECIPE["targets_max"] + 1, w.num_users)
+    return c.astype(np.int32), g.astype(np.int32)
+
+
+def visible_pairs(lengths, c, g, group, window) -> int:
+    """Query-key pairs the mask admits, summed over users (counted row by row from
+    the intervals of each row: context keys, windowed history, own candidate group)."""
+    import numpy as np
+
+    left, right = window
+    assert right == 0
+    total = 0
+    for L, cu_, gu in zip(lengths, c, g):
+        L = int(L)
+        if L == 0:
+            continue
+        cc = min(max(int(cu_), 0), L)
+        gg = min(max(int(gu), 0), L - cc)
+        nc = L - gg
+        i = np.arange(L)
+        lo = np.maximum(cc, i - left) if left >= 0 else np.full(L, cc)
+        hist = np.where(i >= cc, np.maximum(0, np.minimum(i, nc - 1) - lo + 1), 0)
+        ctx = np.where(i < cc, cc, cc)
+        gs = nc + ((i - nc) // group) * group
+        grp = np.where(i >= nc, i - gs + 1, 0)
+        total += int((ctx + hist + grp).sum())
+    return total
+
+
+def run_masked(args, w, dev):
+    """One step = one varlen_causal_attn_fwd_masked call (scheduler + masked kernel)
+    with MASK_RECIPE's per-user counts and window."""
+    import torch
+
+    import varlen_causal_attention_amd as vlca
+
+    qkv = w.qkv_bf16.to(dev)
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    c, g = mask_counts(w)
+    ct, gt = torch.from_numpy(c).to(dev), torch.from_numpy(g).to(dev)
+    out = torch.empty((w.total_tokens, w.n_heads * w.head_dim), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    rec = MASK_RECIPE
+
+    def step():
+        vlca.fwd_masked(qkv, cu, w.max_seqlen, num_contexts=ct, num_targets=gt, target_group_size=rec["group"],
+                        window=rec["window"], n_heads=w.n_heads, scale=w.scale, out=out)
+
+    print(f"[bench] masked {w.name}: T={w.total_tokens} U={w.num_users} recipe={rec}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    pairs = visible_pairs(w.lengths, c, g, rec["group"], rec["window"])
+    flops = 4.0 * w.n_heads * w.head_dim * pairs
+    nbytes = w.algorithmic_bytes()
+    print(f"[bench] masked step {ms_step * 1e3:.2f} us, {pairs} visible pairs per head", file=sys.stderr, flush=True)
+    value = w.total_tokens / (ms_step * 1e-3)
+    print(json.dumps({
+        "metric": "varlen masked attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), HSTU-style mask",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": w.total_tokens, "num_users": w.num_users,
+                   "mask": {k: v for k, v in rec.items() if k != "seed"}, "visible_pairs_per_head": pairs},
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": roofline(flops, nbytes, ms_step * 1e-3, measured_traffic(w.name, "masked"),
+                             "varlen_causal_attn_fwd_masked (scheduler + masked_attention_kernel)"),
+    }), flush=True)
 
 
 def run_backward(args, w, dev):

@@ -71,8 +71,9 @@ enum {
   VLCA_ERR_HIP = -10,            /* a HIP runtime call or kernel launch failed       */
   VLCA_ERR_SCRATCH = -11,        /* varlen_causal_attn_fwd_noalloc: the batch needs a
                                     larger worklist than VLCA_NOALLOC_MAX_ITEMS      */
-  VLCA_ERR_BUCKETS = -12         /* runner bucket sizes not positive and increasing,
+  VLCA_ERR_BUCKETS = -12,        /* runner bucket sizes not positive and increasing,
                                     or more than 64 buckets                          */
+  VLCA_ERR_MASK = -13            /* mask description out of range (see vlca_mask)    */
 };
 
 /*
@@ -122,6 +123,45 @@ enum {
 int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_users,
                            int max_seqlen, int n_heads, int head_dim, float scale,
                            void* out, hipStream_t stream);
+
+/*
+ * HSTU-style mask variants (recsys README, HSTU section: hstu_attn_varlen_func's
+ * num_contexts, num_targets and window_size, and its mask list -- no mask, local
+ * sliding window, causal, contextual + causal, target + causal).  A user of
+ * length L with c = num_contexts[u] context tokens and g = num_targets[u]
+ * candidate tokens at its end (nc = L - g; both clamped to the user) is
+ * [context][history][candidates].  Query row i sees key j of its own user when
+ *   window_right == 0 (causal):
+ *     j < c                                        (every row sees the context),
+ *     i >= c and max(c, lo(i)) <= j <= min(i, nc-1) (history, causal, windowed),
+ *     i >= nc and gs(i) <= j <= i                  (its own candidate group);
+ *     (so a context row sees exactly the context: bidirectional inside it)
+ *   otherwise (num_contexts and num_targets NULL):
+ *     lo(i) <= j <= hi(i),
+ * with lo(i) = max(0, i - window_left) (window_left >= 0; -1 = no bound),
+ * hi(i) = min(L-1, i + window_right) (window_right >= 0; -1 = no bound), and
+ * gs(i) = nc + floor((i - nc) / target_group_size) * target_group_size.
+ */
+typedef struct vlca_mask {
+  const int32_t* num_contexts;  /* device int32 [num_users], or NULL (no context tokens)   */
+  const int32_t* num_targets;   /* device int32 [num_users], or NULL (no candidate tokens) */
+  int target_group_size;        /* >= 1                                                    */
+  int window_left;              /* >= -1                                                   */
+  int window_right;             /* >= -1; must be 0 when num_contexts or num_targets is set */
+} vlca_mask;
+
+/*
+ * Forward with a mask variant.  Arguments and layouts as for
+ * varlen_causal_attn_fwd; mask (host pointer, read during the call) as above.
+ * mask NULL, or the plain causal mask (no contexts, no targets, window (-1, 0)),
+ * runs varlen_causal_attn_fwd itself (same bits).  Other masks run a separate
+ * kernel over the stream's worklist (allocated or grown on first need, never
+ * freed), whose result equals the definition within rounding.  Errors as for
+ * varlen_causal_attn_fwd, plus VLCA_ERR_MASK.
+ */
+int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, int num_users,
+                                  int max_seqlen, int n_heads, int head_dim, float scale,
+                                  const vlca_mask* mask, void* out, hipStream_t stream);
 
 /*
  * Training forward: varlen_causal_attn_fwd (same plan, split decision and output

@@ -218,6 +218,16 @@ hipError_t launch_backward(const void*, const void*, const void*, const float*, 
   return hipSuccess;
 }
 
+hipError_t launch_masked_attention(const void*, const int4* items, const int32_t* count, int32_t*, int n_heads,
+                                   float, const int32_t*, const int32_t*, int group, int wl, int wr, void*, int grid,
+                                   hipStream_t stream) {
+  g.launches.push_back({'m', items, touch(items, count), group, wl, n_heads, grid, wr, {0, 0, 0, nullptr, nullptr},
+                        stream});
+  return hipSuccess;
+}
+
+int masked_blocks_per_cu() { return g.blocks_per_cu; }
+
 int attention_blocks_per_cu(bool) { return g.blocks_per_cu; }
 
 hipError_t noalloc_scratch(char** ptr) {

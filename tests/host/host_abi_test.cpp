@@ -264,6 +264,34 @@ static void test_training_entry_points() {
   CHECK(g.frees == 0 && g.syncs == 0);
 }
 
+static void test_masked_entry_point() {
+  stub::reset();
+  const hipStream_t s = stream_id(12);
+  static int32_t ctx[4], tgt[4];
+  auto fm = [&](const vlca_mask* m, int users, int ms) {
+    return varlen_causal_attn_fwd_masked(QKV, CU, users, ms, 8, 64, 0.125f, m, OUT, s);
+  };
+  vlca_mask bad_group{nullptr, tgt, 0, -1, 0}, bad_left{nullptr, nullptr, 1, -2, 0},
+      bad_right{ctx, nullptr, 1, -1, 3}, bad_right2{nullptr, nullptr, 1, -1, -2};
+  CHECK(fm(&bad_group, 60, 452) == VLCA_ERR_MASK && fm(&bad_left, 60, 452) == VLCA_ERR_MASK);
+  CHECK(fm(&bad_right, 60, 452) == VLCA_ERR_MASK && fm(&bad_right2, 60, 452) == VLCA_ERR_MASK);
+  CHECK(g.launches.empty());
+  // The plain causal mask (or none) is the forward itself.
+  vlca_mask causal{nullptr, nullptr, 1, -1, 0};
+  CHECK(fm(&causal, 60, 452) == VLCA_OK && fm(nullptr, 60, 452) == VLCA_OK);
+  CHECK(g.launches.size() == 2 && g.launches[0].kind == 'f' && g.launches[1].kind == 'f');
+  // A window, contexts and targets: the scheduler, then the masked kernel over its worklist.
+  g.launches.clear();
+  vlca_mask hstu{ctx, tgt, 4, 256, 0};
+  CHECK(fm(&hstu, 60, 452) == VLCA_OK);
+  CHECK(g.launches.size() == 2 && g.launches[0].kind == 's' && g.launches[1].kind == 'm');
+  CHECK(g.launches[1].items == g.launches[0].items && g.launches[1].num_users == 4);
+  CHECK(g.launches[1].max_tiles == 256 && g.launches[1].layer_log2 == 0 && g.launches[1].grid == 1024);
+  vlca_mask bidir{nullptr, nullptr, 1, -1, -1};
+  CHECK(fm(&bidir, 60, 452) == VLCA_OK && g.launches.back().kind == 'm' && g.launches.back().layer_log2 == -1);
+  CHECK(g.frees == 0 && g.syncs == 0);
+}
+
 int main() {
   setvbuf(stdout, nullptr, _IONBF, 0);
   test_argument_errors();
@@ -273,6 +301,7 @@ int main() {
   test_noalloc_entry_point();
   test_graph_runner();
   test_training_entry_points();
+  test_masked_entry_point();
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
 }

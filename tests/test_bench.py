@@ -55,3 +55,16 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_visible_pairs_of_the_mask_recipe():
+    import numpy as np
+
+    import oracle
+    # counted against the oracle's dense mask on a few users (the oracle is test infrastructure)
+    lengths, c, g = [5, 40, 1, 0, 300], [2, 16, 1, 0, 9], [1, 30, 0, 0, 32]
+    want = sum(int(oracle.hstu_mask(L, min(cc, L), min(gg, L - min(cc, L)), 8, (256, 0)).sum())
+               for L, cc, gg in zip(lengths, c, g) if L > 0)
+    assert bench.visible_pairs(lengths, c, g, 8, (256, 0)) == want
+    # no context, no candidates, no window bound: the causal triangle
+    assert bench.visible_pairs([10, 7], [0, 0], [0, 0], 1, (-1, 0)) == 55 + 28

@@ -13,7 +13,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "VlcaError", "library", "library_path", "fwd", "fwd_noalloc", "fwd_lse", "bwd", "attention",
+    "VlcaError", "library", "library_path", "fwd", "fwd_masked", "fwd_noalloc", "fwd_lse", "bwd", "attention",
     "build_worklist", "fwd_with_worklist",
     "worklist_capacity", "single_kernel", "tile_rows", "strerror", "call_module", "EXPORTED_SYMBOLS",
     "GraphRunner", "PAGES_BUCKETS",
@@ -27,6 +27,7 @@ _call = None  # the CPython trampoline for fwd / fwd_worklist (ctypes when it is
 EXPORTED_SYMBOLS = (
     "varlen_causal_attn_fwd",
     "varlen_causal_attn_fwd_lse",
+    "varlen_causal_attn_fwd_masked",
     "varlen_causal_attn_bwd",
     "varlen_causal_attn_fwd_noalloc",
     "varlen_causal_attn_worklist_capacity",
@@ -41,6 +42,12 @@ EXPORTED_SYMBOLS = (
     "varlen_causal_attn_tile_rows",
     "varlen_causal_attn_strerror",
 )
+
+
+class _Mask(ctypes.Structure):
+    """Mirror of ``vlca_mask`` (include/varlen_causal_attn.h)."""
+    _fields_ = [("num_contexts", ctypes.c_void_p), ("num_targets", ctypes.c_void_p),
+                ("target_group_size", ctypes.c_int), ("window_left", ctypes.c_int), ("window_right", ctypes.c_int)]
 
 
 class VlcaError(RuntimeError):
@@ -67,6 +74,9 @@ def library():
     lib.varlen_causal_attn_fwd.restype = c_int
     lib.varlen_causal_attn_fwd_lse.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp, vp]
     lib.varlen_causal_attn_fwd_lse.restype = c_int
+    lib.varlen_causal_attn_fwd_masked.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float,
+                                                  ctypes.POINTER(_Mask), vp, vp]
+    lib.varlen_causal_attn_fwd_masked.restype = c_int
     lib.varlen_causal_attn_bwd.argtypes = [vp, vp, vp, vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
     lib.varlen_causal_attn_bwd.restype = c_int
     lib.varlen_causal_attn_fwd_noalloc.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
@@ -211,6 +221,36 @@ def fwd(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,
     rc = _call.fwd(*args) if _call is not None else lib.varlen_causal_attn_fwd(*args)
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd")
+    return out
+
+
+def fwd_masked(qkv, cu_seqlens, max_seqlen: int, num_contexts=None, num_targets=None, target_group_size: int = 1,
+               window=(-1, 0), n_heads: int = 8, head_dim: int = 64, scale: Optional[float] = None, out=None):
+    """Forward with the HSTU-style mask variants (``vlca_mask``): per-user context and
+    candidate counts (int32 device tensors [num_users] or None), the candidates'
+    group size, and ``window = (left, right)`` (-1: unbounded; right 0: causal)."""
+    torch = _torch_mod()
+    _check_qkv(qkv, n_heads, head_dim)
+    cu = _check_cu(cu_seqlens)
+    users = cu.shape[0] - 1
+    ptrs = []
+    for name, t in (("num_contexts", num_contexts), ("num_targets", num_targets)):
+        if t is None:
+            ptrs.append(None)
+            continue
+        if (t.dtype != torch.int32 or not t.is_cuda or t.dim() != 1 or t.shape[0] != users
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 device tensor of {users} entries")
+        ptrs.append(t.data_ptr())
+    out = _out_tensor(qkv, n_heads, head_dim, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    m = _Mask(ptrs[0], ptrs[1], int(target_group_size), int(window[0]), int(window[1]))
+    rc = library().varlen_causal_attn_fwd_masked(qkv.data_ptr(), cu.data_ptr(), users, int(max_seqlen), int(n_heads),
+                                                 int(head_dim), float(scale), ctypes.byref(m), out.data_ptr(),
+                                                 _stream_handle(qkv.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_fwd_masked")
     return out
 
 

@@ -307,6 +307,43 @@ int varlen_causal_attn_fwd_lse(const void* qkv, const int32_t* cu_seqlens, int n
   if (num_users > 0 && max_seqlen > 0 && lse == nullptr) return VLCA_ERR_NULL_POINTER;
   return fwd_impl(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out, lse, stream);
 }
+int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
+                                  int n_heads, int head_dim, float scale, const vlca_mask* mask, void* out,
+                                  hipStream_t stream) {
+  if (mask != nullptr) {
+    if (mask->target_group_size < 1 || mask->window_left < -1 || mask->window_right < -1) return VLCA_ERR_MASK;
+    if ((mask->num_contexts != nullptr || mask->num_targets != nullptr) && mask->window_right != 0)
+      return VLCA_ERR_MASK;
+  }
+  const bool plain = mask == nullptr || (mask->num_contexts == nullptr && mask->num_targets == nullptr &&
+                                         mask->window_left == -1 && mask->window_right == 0);
+  if (plain) return fwd_impl(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out, nullptr, stream);
+  int rc = check_attention_args(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out);
+  if (rc != VLCA_OK) return rc;
+  if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  const int64_t need = required_capacity(num_users, max_seqlen);
+  StreamState st;
+  rc = get_workspace(dev, stream, need, &st);
+  if (rc != VLCA_OK) return rc;
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  int32_t* count = workspace_count(&st);
+  int32_t* queue = count + vlca::kQueueStride;
+  if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, st.items, count, queue,
+                            vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
+    return VLCA_ERR_HIP;
+  int64_t g = static_cast<int64_t>(cu_count(dev)) * vlca::masked_blocks_per_cu();
+  g = std::min<int64_t>(g, vlca::kMaxGrid);
+  g -= g % 8;
+  g = std::max<int64_t>(std::min<int64_t>(g, need * n_heads), 1);
+  if (vlca::launch_masked_attention(qkv, st.items, count, queue, n_heads, scale * kLog2e, mask->num_contexts,
+                                    mask->num_targets, mask->target_group_size, mask->window_left,
+                                    mask->window_right, out, static_cast<int>(g), stream) != hipSuccess)
+    return VLCA_ERR_HIP;
+  return VLCA_OK;
+}
+
 int varlen_causal_attn_bwd(const void* qkv, const void* out, const void* dout, const float* lse,
                            const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, int head_dim,
                            float scale, void* dqkv, hipStream_t stream) {
@@ -434,6 +471,7 @@ const char* varlen_causal_attn_strerror(int code) {
     case VLCA_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case VLCA_ERR_SCRATCH: return "batch needs more worklist items than the no-allocation scratch holds";
     case VLCA_ERR_BUCKETS: return "bucket sizes must be positive and strictly increasing (at most 64 buckets)";
+    case VLCA_ERR_MASK: return "mask out of range (group size >= 1, windows >= -1, contexts/targets need window_right 0)";
     default: return "unknown error code";
   }
 }

@@ -88,29 +88,6 @@ struct Assign {
   }
 };
 
-// The wave's 16 rows of a 64 x 64 fp32 result held in the MFMA C layout of a
-// transposed product (lane (g, lq): dims 16 d + 4 g + r of row lq) times `mul`,
-// rounded to bf16, staged through the wave's own 2 KB of LDS at `rows`, and
-// stored as full 128-byte rows: row i goes to dst + i * ld if i < nvalid.
-__device__ __forceinline__ void store_rows(LDS char* rows, const f32x4 (&acc)[4], float mul, uint16_t* dst, int64_t ld,
-                                           int nvalid) {
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));
-  const int lq = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const u32x2 wv = {pack_bf16x2(acc[d][0] * mul, acc[d][1] * mul), pack_bf16x2(acc[d][2] * mul, acc[d][3] * mul)};
-    *(LDS u32x2*)(rows + lq * 128 + (((2 * d + (g >> 1)) ^ swz(lq)) << 4) + 8 * (g & 1)) = wv;
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * i + (lane >> 3), c = lane & 7;
-    const u32x4 v = *(const LDS u32x4*)(rows + r * 128 + ((c ^ swz(r)) << 4));
-    if (r < nvalid) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + r * ld + 8 * c));
-  }
-}
-
 // ------------------------------------------------------------- preprocess
 
 // D[t, h] = sum_d dO[t, h, d] * O[t, h, d] (fp32) for every row t < T =

@@ -28,6 +28,9 @@ constexpr int kWaves = 4;                              // wave w owns rows 16w .
 constexpr int kAttnThreads = 64 * kWaves;
 constexpr int kTileBytes = kTileRows * kHeadDim * 2;  // 8 KB: one 64 x 64 bf16 tile, 128 B rows
 constexpr int kStageBytes = 2 * kTileBytes;           // two tiles (K then V, or Q then dO)
+// The running max of a query is raised only when a key exceeds it by more than
+// 2^kRescaleLog2 in exp2 units.
+constexpr float kRescaleLog2 = 8.0f;
 
 // XOR swizzle of the 16-byte chunk index inside a 128-byte LDS tile row: chunk
 // c of row r is stored at chunk c ^ (r % 8).  With the fragment row orders below
@@ -156,6 +159,127 @@ __device__ __forceinline__ void make_lanes(Lanes& L, int64_t ldq) {
 // Wait for this wave's LDS operations, then a workgroup barrier (no wait on
 // copies in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Online-softmax state of one lane: the running reference max m (raw score
+// units), the O^T accumulator (dims 16d + 4g + r) and the denominator (every
+// register of l holds it).
+struct Acc {
+  float m;
+  float moff;  // -m * sl2: the exponent offset of the weights
+  float mthr;  // m + rescale threshold: keys above it raise m
+  f32x4 o[4];
+  f32x4 l;
+};
+
+// Masks of a tile step: which of the lane's 16 keys of a tile (key 16 b + 4 g + r
+// of lane group g) its query sees.
+struct NoMask {  // every key
+  static constexpr bool kAny = false;
+  __device__ bool operator()(int, int) const { return true; }
+};
+struct DiagMask {  // keys up to lim (the lane's query row on the diagonal tile)
+  static constexpr bool kAny = true;
+  int lim, g;
+  __device__ bool operator()(int b, int r) const { return 16 * b + 4 * g + r <= lim; }
+};
+
+// One key tile of one item: S^T = K Q^T, mask, softmax update, O^T += V^T P^T
+// and l += 1^T P^T.  Masked keys score -inf.  kSafe: a query may see no key of
+// the tile's first half (or of the tiles so far) -- its running max is then still
+// -inf, and the rescale factor and weight offset are taken as 1 and 0 instead of
+// the NaN that -inf - (-inf) gives; without kSafe the caller guarantees that the
+// first half of the first tile holds a visible key of every query.
+template <bool kSafe = false, typename Mask>
+__device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2],
+                                          const bf16x8& ones, float sl2, float rescale_thr, Acc& A,
+                                          const Mask& mask) {
+  f32x4 s[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const bf16x8 k0 = lds_b128(base, L.kofs[0] + 2048 * b);
+    const bf16x8 k1 = lds_b128(base, L.kofs[1] + 2048 * b);
+    s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[b], 0, 0, 0);
+  }
+  if constexpr (Mask::kAny) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!mask(b, r)) s[b][r] = -__builtin_inff();
+  }
+  // The tile is taken in two halves of 32 keys (score blocks 2hh, 2hh+1), so the
+  // second half's QK^T MFMAs run while the first half's softmax is computed.
+  // Lane-local max over this lane's 8 keys of the half.  The reference max m of a
+  // query is shared by its 4 lane groups; only when some key exceeds it by more
+  // than the threshold (and on the first tile, m = -inf; the first half always
+  // holds a visible key of every query) is the true max formed across the lane
+  // groups and m raised, with the accumulators rescaled.  The common path needs
+  // no cross-lane traffic.
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const f32x4& s0 = s[2 * hh];
+    const f32x4& s1 = s[2 * hh + 1];
+    const float lm = vmax(vmax(vmax(vmax(s0[0], s0[1]), s0[2]), vmax(vmax(s0[3], s1[0]), s1[1])), vmax(s1[2], s1[3]));
+    if (__any(lm > A.mthr)) {  // wave-uniform
+      const float mt = max_across_lane_groups(lm);
+      const float mn = fmaxf(A.m, mt);
+      const bool none = kSafe && mn == -__builtin_inff();  // no visible key yet
+      const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f((A.m - mn) * sl2);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) A.o[d] *= alpha;
+      A.l *= alpha;
+      A.m = mn;
+      A.moff = none ? 0.0f : -mn * sl2;
+      A.mthr = mn + rescale_thr;
+    }
+    const float moff = A.moff;
+    // P^T slots 0..3 of lane group g = keys 32hh + 4g + 0..3 (block 2hh), slots
+    // 4..7 = keys 32hh + 16 + 4g + 0..3 (block 2hh+1)
+    uint4 pw;
+    pw.x = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
+    pw.y = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s0[3], sl2, moff)));
+    pw.z = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[0], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[1], sl2, moff)));
+    pw.w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2], sl2, moff)),
+                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[3], sl2, moff)));
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bf16x4 lo = lds_tr16(base, L.vofs[d] + 4096 * hh);
+      const bf16x4 hi = lds_tr16(base, L.vofs[d] + 4096 * hh + 2048);
+      const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      A.o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, A.o[d], 0, 0, 0);
+    }
+    A.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, A.l, 0, 0, 0);
+  }
+}
+
+// The wave's 16 rows of a 64 x 64 fp32 result held in the MFMA C layout of a
+// transposed product (lane (g, lq): dims 16 d + 4 g + r of row lq) times `mul`
+// (per lane, i.e. per row),
+// rounded to bf16, staged through the wave's own 2 KB of LDS at `rows`, and
+// stored as full 128-byte rows: row i goes to dst + i * ld if i < nvalid.
+__device__ __forceinline__ void store_rows(LDS char* rows, const f32x4 (&acc)[4], float mul, uint16_t* dst, int64_t ld,
+                                           int nvalid) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int lq = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x2 wv = {pack_bf16x2(acc[d][0] * mul, acc[d][1] * mul), pack_bf16x2(acc[d][2] * mul, acc[d][3] * mul)};
+    *(LDS u32x2*)(rows + lq * 128 + (((2 * d + (g >> 1)) ^ swz(lq)) << 4) + 8 * (g & 1)) = wv;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * i + (lane >> 3), c = lane & 7;
+    const u32x4 v = *(const LDS u32x4*)(rows + r * 128 + ((c ^ swz(r)) << 4));
+    if (r < nvalid) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + r * ld + 8 * c));
+  }
+}
 
 }  // namespace
 }  // namespace vlca

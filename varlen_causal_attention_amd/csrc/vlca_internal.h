@@ -86,6 +86,15 @@ hipError_t launch_backward(const void* qkv, const void* out, const void* dout, c
                            const int32_t* cu_seqlens, int num_users, const int4* items, const int32_t* count,
                            int64_t max_items, int n_heads, float scale, void* dqkv, int cus, hipStream_t stream);
 
+// The forward with the HSTU-style mask variants (vlca_masked.hip) over the
+// scheduler's worklist of whole items, claiming items from the zeroed counters
+// at queue.  num_contexts / num_targets: device [num_users] or null.
+hipError_t launch_masked_attention(const void* qkv, const int4* items, const int32_t* count, int32_t* queue,
+                                   int n_heads, float scale_log2e, const int32_t* num_contexts,
+                                   const int32_t* num_targets, int group, int window_left, int window_right,
+                                   void* out, int grid, hipStream_t stream);
+int masked_blocks_per_cu();
+
 // Fixed-length offsets for a captured graph: out[i] = min(cu_seqlens[min(i,
 // num_users)], total) for i = 0 .. max_users (num_users <= max_users).
 hipError_t launch_pad_offsets(const int32_t* cu_seqlens, int num_users, int total, int32_t* out, int max_users,

@@ -56,7 +56,6 @@ namespace {
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedCache = 8160;  // cu_seqlens entries cached in LDS by the scheduler (LDS <= 64 KB)
-constexpr float kRescaleLog2 = 8.0f;
 
 // ----------------------------------------------------------------- scheduler
 
@@ -327,86 +326,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
 
 // ----------------------------------------------------------------- attention
 
-// Online-softmax state of one lane: the running reference max m (raw score
-// units), the O^T accumulator (dims 16d + 4g + r) and the denominator (every
-// register of l holds it).
-struct Acc {
-  float m;
-  float moff;  // -m * sl2: the exponent offset of the weights
-  float mthr;  // m + rescale threshold: keys above it raise m
-  f32x4 o[4];
-  f32x4 l;
-};
-
-// One key tile of one item: S^T = K Q^T, mask (diagonal tile only), softmax
-// update, O^T += V^T P^T and l += 1^T P^T.
-// kDiag: keys kk > lim are masked (lim = the lane's query row on the diagonal
-// tile; 63 or more masks nothing).
-template <bool kDiag>
-__device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2],
-                                          const bf16x8& ones, float sl2, float rescale_thr, Acc& A, int lim = 0) {
-  f32x4 s[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const bf16x8 k0 = lds_b128(base, L.kofs[0] + 2048 * b);
-    const bf16x8 k1 = lds_b128(base, L.kofs[1] + 2048 * b);
-    s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[b], 0, 0, 0);
-  }
-  if (kDiag) {  // key kk visible iff kk <= lim (on the diagonal tile, lim = qr)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * b + 4 * L.g + r > lim) s[b][r] = -__builtin_inff();
-  }
-  // The tile is taken in two halves of 32 keys (score blocks 2hh, 2hh+1), so the
-  // second half's QK^T MFMAs run while the first half's softmax is computed.
-  // Lane-local max over this lane's 8 keys of the half.  The reference max m of a
-  // query is shared by its 4 lane groups; only when some key exceeds it by more
-  // than the threshold (and on the first tile, m = -inf; the first half always
-  // holds a visible key of every query) is the true max formed across the lane
-  // groups and m raised, with the accumulators rescaled.  The common path needs
-  // no cross-lane traffic.
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const f32x4& s0 = s[2 * hh];
-    const f32x4& s1 = s[2 * hh + 1];
-    const float lm = vmax(vmax(vmax(vmax(s0[0], s0[1]), s0[2]), vmax(vmax(s0[3], s1[0]), s1[1])), vmax(s1[2], s1[3]));
-    if (__any(lm > A.mthr)) {  // wave-uniform
-      const float mt = max_across_lane_groups(lm);
-      const float mn = fmaxf(A.m, mt);
-      const float alpha = __builtin_amdgcn_exp2f((A.m - mn) * sl2);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) A.o[d] *= alpha;
-      A.l *= alpha;
-      A.m = mn;
-      A.moff = -mn * sl2;
-      A.mthr = mn + rescale_thr;
-    }
-    const float moff = A.moff;
-    // P^T slots 0..3 of lane group g = keys 32hh + 4g + 0..3 (block 2hh), slots
-    // 4..7 = keys 32hh + 16 + 4g + 0..3 (block 2hh+1)
-    uint4 pw;
-    pw.x = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0], sl2, moff)),
-                       __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
-    pw.y = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2], sl2, moff)),
-                       __builtin_amdgcn_exp2f(__builtin_fmaf(s0[3], sl2, moff)));
-    pw.z = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[0], sl2, moff)),
-                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[1], sl2, moff)));
-    pw.w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2], sl2, moff)),
-                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[3], sl2, moff)));
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const bf16x4 lo = lds_tr16(base, L.vofs[d] + 4096 * hh);
-      const bf16x4 hi = lds_tr16(base, L.vofs[d] + 4096 * hh + 2048);
-      const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      A.o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, A.o[d], 0, 0, 0);
-    }
-    A.l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, A.l, 0, 0, 0);
-  }
-}
 
 
 // The launch condition of the single-kernel plan counts whole items
@@ -853,26 +772,26 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
     for (; j + 2 < khi; j += 2) {
       wait_and_barrier<0>();
       issue_tile(kStageBytes, j + 1);
-      tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
+      tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
       wait_and_barrier<0>();
       issue_tile(0, j + 2);
-      tile_step<false>(st1, L, qf, ones, sl2, rescale_thr, A);
+      tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
     }
     if (j + 1 < khi) {  // two tiles left: j in stage 0, the last one goes to stage 1
       wait_and_barrier<0>();
       issue_tile(kStageBytes, j + 1);
-      tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
+      tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
       wait_and_barrier<0>();
       if (diag_last)
-        tile_step<true>(st1, L, qf, ones, sl2, rescale_thr, A, L.qr);
+        tile_step(st1, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g});
       else
-        tile_step<false>(st1, L, qf, ones, sl2, rescale_thr, A);
+        tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
     } else {  // one tile left, in stage 0
       wait_and_barrier<0>();
       if (diag_last)
-        tile_step<true>(st0, L, qf, ones, sl2, rescale_thr, A, L.qr);
+        tile_step(st0, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g});
       else
-        tile_step<false>(st0, L, qf, ones, sl2, rescale_thr, A);
+        tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
     }
     // The claim made at the item's start is passed on; every wave read s_next
     // before this item's first barrier.
