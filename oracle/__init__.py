@@ -18,6 +18,8 @@ Contents:
                                       block-diagonal causal mask built from the offsets
   attention.block_diagonal_causal_mask
   worklist.reference_worklist         the segment scheduler's (user, q-tile) order
+  layer.layer_norm, layer.linear, layer.attention_block  the layer's attention sub-block around
+                                      the op (LayerNorm -> Linear_qkv -> attention -> Linear_out + residual)
 
 Every function is pinned by ``tests/test_oracle.py`` to something other than
 itself (brute force, closed forms, invariants, a library routine on the
@@ -35,4 +37,5 @@ from .attention import (  # noqa: F401
     varlen_causal_attention_lse,
     varlen_causal_attention_rows,
 )
+from .layer import attention_block, layer_norm, linear  # noqa: F401
 from .worklist import reference_worklist, tiles_per_user  # noqa: F401

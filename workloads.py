@@ -150,6 +150,46 @@ def draw_dout(total_tokens: int, n_heads: int = N_HEADS, seed: int = 1):
     return draw_qkv(rng, total_tokens, cols=n_heads * HEAD_DIM)
 
 
+@dataclasses.dataclass
+class LayerParams:
+    """Synthetic parameters of the layer's attention sub-block (bf16 torch CPU
+    tensors, nn.Linear layout [out, in]): no trained weights exist here."""
+    gamma: "object"
+    beta: "object"
+    w_qkv: "object"
+    b_qkv: "object"
+    w_out: "object"
+    b_out: "object"
+    eps: float = 1e-5
+
+
+def make_layer_params(d_model: int = OUT_COLS, n_heads: int = N_HEADS, seed: int = 3) -> LayerParams:
+    """gamma ~ 1 + 0.1 N(0,1), beta ~ 0.1 N(0,1), weights ~ N(0, 1/d_model) (unit
+    variance through each product), biases ~ 0.1 N(0,1); rounded to bf16."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+
+    def bf16(a):
+        return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+    n_qkv = 3 * n_heads * HEAD_DIM
+    return LayerParams(
+        gamma=bf16(1.0 + 0.1 * rng.standard_normal(d_model)),
+        beta=bf16(0.1 * rng.standard_normal(d_model)),
+        w_qkv=bf16(rng.standard_normal((n_qkv, d_model)) / np.sqrt(d_model)),
+        b_qkv=bf16(0.1 * rng.standard_normal(n_qkv)),
+        w_out=bf16(rng.standard_normal((d_model, n_heads * HEAD_DIM)) / np.sqrt(n_heads * HEAD_DIM)),
+        b_out=bf16(0.1 * rng.standard_normal(d_model)),
+    )
+
+
+def draw_layer_input(total_tokens: int, d_model: int = OUT_COLS, seed: int = 2):
+    """The layer input x: N(0,1) float32 draws [total_tokens, d_model] rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    return draw_qkv(rng, total_tokens, cols=d_model)
+
+
 def make_config(idx: int, seed: int = 0, with_values: bool = True) -> Workload:
     rng = np.random.default_rng(seed)
     lengths, max_seqlen, vscale = config_lengths(idx, rng)
