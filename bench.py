@@ -33,9 +33,11 @@ KERNEL_SOURCES = {
     "fwd": ("vlca_device.h", "vlca_kernels.hip"),
     "bwd": ("vlca_device.h", "vlca_kernels.hip", "vlca_backward.hip"),
     "masked": ("vlca_device.h", "vlca_kernels.hip", "vlca_masked.hip"),
+    "layer": ("vlca_device.h", "vlca_kernels.hip", "vlca_proj.hip"),
 }
 ATTN_KERNEL = "attention_kernel"  # <true, true, false>: single-kernel plan; <false, ...>: over a worklist
-PROFILE_PREFIX = {"fwd": "attention_kernel", "bwd": "backward", "masked": "masked_attention_kernel"}
+PROFILE_PREFIX = {"fwd": "attention_kernel", "bwd": "backward", "masked": "masked_attention_kernel",
+                  "layer": "attention_block"}
 
 
 def kernel_source_hash(mode: str = "fwd") -> str:
@@ -325,9 +327,10 @@ def main():
     # batch read 48.4 us, with 2000 42.7 us).
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = 6823 tokens / 60 users)")
-    ap.add_argument("--mode", choices=("fwd", "bwd", "masked"), default="fwd",
+    ap.add_argument("--mode", choices=("fwd", "bwd", "masked", "layer"), default="fwd",
                     help="fwd: the forward (the default measurement); bwd: the training backward; "
-                         "masked: the forward with an HSTU-style mask (MASK_RECIPE)")
+                         "masked: the forward with an HSTU-style mask (MASK_RECIPE); layer: the attention "
+                         "sub-block (LayerNorm + Linear_qkv, attention, Linear_out + residual)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -374,6 +377,9 @@ def main():
         return
     if args.mode == "masked":
         run_masked(args, w, dev)
+        return
+    if args.mode == "layer":
+        run_layer(args, w, dev)
         return
     qkv = w.qkv_bf16.to(dev)
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
@@ -566,6 +572,83 @@ def run_masked(args, w, dev):
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": roofline(flops, nbytes, ms_step * 1e-3, measured_traffic(w.name, "masked"),
                              "varlen_causal_attn_fwd_masked (scheduler + masked_attention_kernel)"),
+    }), flush=True)
+
+
+def _time(step, args, stream):
+    import torch
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps
+
+
+def run_layer(args, w, dev):
+    """One step = the layer's attention sub-block: varlen_causal_attn_ln_qkv
+    (LayerNorm fused into the qkv product), varlen_causal_attn_fwd and
+    varlen_causal_attn_out_residual (bias and residual fused into the output
+    product), on synthetic layer parameters.  Each product is also timed alone;
+    the roofline object is the qkv product's (the largest of the three)."""
+    import torch
+
+    import varlen_causal_attention_amd as vlca
+    import workloads
+
+    p = workloads.make_layer_params()
+    gp = {k: getattr(p, k).to(dev) for k in ("gamma", "beta", "w_qkv", "b_qkv", "w_out", "b_out")}
+    x = workloads.draw_layer_input(w.total_tokens).to(dev)
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    T = w.total_tokens
+    qkv = torch.empty((T, 1536), dtype=torch.bfloat16, device=dev)
+    attn = torch.empty((T, 512), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, 512), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def ln_step():
+        vlca.ln_qkv(x, gp["gamma"], gp["beta"], gp["w_qkv"], gp["b_qkv"], eps=p.eps, out=qkv)
+
+    def attn_step():
+        vlca.fwd(qkv, cu, w.max_seqlen, scale=w.scale, out=attn)
+
+    def out_step():
+        vlca.out_residual(attn, gp["w_out"], gp["b_out"], x, out=y)
+
+    def block():
+        ln_step()
+        attn_step()
+        out_step()
+
+    print(f"[bench] attention sub-block {w.name}: T={T}", file=sys.stderr, flush=True)
+    ms_block = _time(block, args, stream)
+    ms_ln = _time(ln_step, args, stream)
+    ms_out = _time(out_step, args, stream)
+    print(f"[bench] sub-block {ms_block * 1e3:.2f} us; ln_qkv {ms_ln * 1e3:.2f} us; out_residual "
+          f"{ms_out * 1e3:.2f} us", file=sys.stderr, flush=True)
+    f_qkv = 2.0 * T * 512 * 1536
+    f_out = 2.0 * T * 512 * 512
+    b_qkv = T * (512 + 1536) * 2 + 1536 * 512 * 2 + 2 * 512 * 2 + 1536 * 2  # x, qkv, weights, gamma/beta, bias
+    b_out = T * (512 * 3) * 2 + 512 * 512 * 2 + 512 * 2                      # attn, residual, y, weights, bias
+    flops = f_qkv + w.causal_flops() + f_out
+    value = T / (ms_block * 1e-3)
+    print(json.dumps({
+        "metric": "packed layer attention sub-block tokens/s (LayerNorm+Linear_qkv, attention, Linear_out+residual)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_block, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random layer parameters)",
+        "config": {"workload": w.name, "total_tokens": T, "num_users": w.num_users, "d_model": 512, "n_heads": 8},
+        "tflops": flops / (ms_block * 1e-3) / 1e12,
+        "ln_qkv_us": ms_ln * 1e3, "out_residual_us": ms_out * 1e3,
+        "roofline": roofline(f_qkv, b_qkv, ms_ln * 1e-3, measured_traffic(w.name, "layer"),
+                             "proj_kernel<true, false> (LayerNorm + Linear_qkv)"),
+        "out_residual_roofline": roofline(f_out, b_out, ms_out * 1e-3, None,
+                                          "proj_kernel<false, true> (Linear_out + bias + residual)"),
     }), flush=True)
 
 

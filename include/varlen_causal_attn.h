@@ -73,7 +73,9 @@ enum {
                                     larger worklist than VLCA_NOALLOC_MAX_ITEMS      */
   VLCA_ERR_BUCKETS = -12,        /* runner bucket sizes not positive and increasing,
                                     or more than 64 buckets                          */
-  VLCA_ERR_MASK = -13            /* mask description out of range (see vlca_mask)    */
+  VLCA_ERR_MASK = -13,           /* mask description out of range (see vlca_mask)    */
+  VLCA_ERR_SHAPE = -14           /* neighbour kernels: d_model != 512, or an output
+                                    width that is not a positive multiple of 128     */
 };
 
 /*
@@ -162,6 +164,35 @@ typedef struct vlca_mask {
 int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, int num_users,
                                   int max_seqlen, int n_heads, int head_dim, float scale,
                                   const vlca_mask* mask, void* out, hipStream_t stream);
+
+/*
+ * The attention's neighbours in the packed Transformer layer (cti2026 README,
+ * Transformer-layer listing: residual = x; x = LayerNorm(x); qkv = Linear_qkv(x);
+ * attn_out = FlashAttention_Varlen(qkv, user_offsets); x = residual +
+ * Linear_out(attn_out)), with their elementwise work fused into the products.
+ * All tensors bf16, row-major, device, caller-owned; T = total_tokens rows;
+ * weights in nn.Linear's layout [out_features, in_features]; fp32 accumulation,
+ * one rounding to bf16 of each output.  d_model must be 512.
+ *
+ * varlen_causal_attn_ln_qkv: qkv[T, n_out] = LayerNorm(x)[T, 512] w[n_out, 512]^T
+ * + b[n_out], LayerNorm(x) = (x - mean) / sqrt(var + eps) * gamma + beta over each
+ * row's 512 columns (population variance), rounded to bf16 before the product.
+ * n_out = 3 * n_heads * 64 gives the forward's qkv layout; a positive multiple
+ * of 128.  qkv must not overlap x.
+ */
+int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta, float eps,
+                              const void* w_qkv, const void* b_qkv, int total_tokens, int d_model,
+                              int n_out, void* qkv, hipStream_t stream);
+
+/*
+ * varlen_causal_attn_out_residual: y[T, n_out] = residual[T, n_out] +
+ * attn[T, 512] w[n_out, 512]^T + b[n_out] (n_out = d_model = 512 in the layer; a
+ * positive multiple of 128).  y may be residual itself (each element is read
+ * before it is written, by the same thread) but not attn.
+ */
+int varlen_causal_attn_out_residual(const void* attn, const void* w_out, const void* b_out,
+                                    const void* residual, int total_tokens, int d_model, int n_out,
+                                    void* y, hipStream_t stream);
 
 /*
  * Training forward: varlen_causal_attn_fwd (same plan, split decision and output

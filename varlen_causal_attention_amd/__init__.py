@@ -14,6 +14,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "VlcaError", "library", "library_path", "fwd", "fwd_masked", "fwd_noalloc", "fwd_lse", "bwd", "attention",
+    "ln_qkv", "out_residual", "attention_block",
     "build_worklist", "fwd_with_worklist",
     "worklist_capacity", "single_kernel", "tile_rows", "strerror", "call_module", "EXPORTED_SYMBOLS",
     "GraphRunner", "PAGES_BUCKETS",
@@ -29,6 +30,8 @@ EXPORTED_SYMBOLS = (
     "varlen_causal_attn_fwd_lse",
     "varlen_causal_attn_fwd_masked",
     "varlen_causal_attn_bwd",
+    "varlen_causal_attn_ln_qkv",
+    "varlen_causal_attn_out_residual",
     "varlen_causal_attn_fwd_noalloc",
     "varlen_causal_attn_worklist_capacity",
     "varlen_causal_attn_build_worklist",
@@ -77,6 +80,10 @@ def library():
     lib.varlen_causal_attn_fwd_masked.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float,
                                                   ctypes.POINTER(_Mask), vp, vp]
     lib.varlen_causal_attn_fwd_masked.restype = c_int
+    lib.varlen_causal_attn_ln_qkv.argtypes = [vp, vp, vp, c_float, vp, vp, c_int, c_int, c_int, vp, vp]
+    lib.varlen_causal_attn_ln_qkv.restype = c_int
+    lib.varlen_causal_attn_out_residual.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, vp, vp]
+    lib.varlen_causal_attn_out_residual.restype = c_int
     lib.varlen_causal_attn_bwd.argtypes = [vp, vp, vp, vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
     lib.varlen_causal_attn_bwd.restype = c_int
     lib.varlen_causal_attn_fwd_noalloc.argtypes = [vp, i32p, c_int, c_int, c_int, c_int, c_float, vp, vp]
@@ -252,6 +259,61 @@ def fwd_masked(qkv, cu_seqlens, max_seqlen: int, num_contexts=None, num_targets=
     if rc != 0:
         raise VlcaError(rc, "varlen_causal_attn_fwd_masked")
     return out
+
+
+def _check_bf16(name, t, shape, device):
+    torch = _torch_mod()
+    if (tuple(t.shape) != tuple(shape) or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda
+            or (device.index is not None and t.get_device() != device.index)):
+        raise ValueError(f"{name} must be a contiguous bfloat16 device tensor of shape {tuple(shape)}")
+
+
+def ln_qkv(x, gamma, beta, w_qkv, b_qkv, eps: float = 1e-5, out=None):
+    """qkv = LayerNorm(x) w_qkv^T + b_qkv (x bf16 [T, 512]; w_qkv [n_out, 512] as nn.Linear stores it)."""
+    torch = _torch_mod()
+    T, d = x.shape
+    n_out = w_qkv.shape[0]
+    for name, t, shape in (("x", x, (T, d)), ("gamma", gamma, (d,)), ("beta", beta, (d,)),
+                           ("w_qkv", w_qkv, (n_out, d)), ("b_qkv", b_qkv, (n_out,))):
+        _check_bf16(name, t, shape, x.device)
+    if out is None:
+        out = torch.empty((T, n_out), dtype=torch.bfloat16, device=x.device)
+    _check_bf16("out", out, (T, n_out), x.device)
+    rc = library().varlen_causal_attn_ln_qkv(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps),
+                                             w_qkv.data_ptr(), b_qkv.data_ptr(), T, d, n_out, out.data_ptr(),
+                                             _stream_handle(x.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_ln_qkv")
+    return out
+
+
+def out_residual(attn, w_out, b_out, residual, out=None):
+    """y = residual + attn w_out^T + b_out (attn bf16 [T, 512]; w_out [n_out, 512])."""
+    torch = _torch_mod()
+    T, d = attn.shape
+    n_out = w_out.shape[0]
+    for name, t, shape in (("attn", attn, (T, d)), ("w_out", w_out, (n_out, d)), ("b_out", b_out, (n_out,)),
+                           ("residual", residual, (T, n_out))):
+        _check_bf16(name, t, shape, attn.device)
+    if out is None:
+        out = torch.empty((T, n_out), dtype=torch.bfloat16, device=attn.device)
+    _check_bf16("out", out, (T, n_out), attn.device)
+    rc = library().varlen_causal_attn_out_residual(attn.data_ptr(), w_out.data_ptr(), b_out.data_ptr(),
+                                                   residual.data_ptr(), T, d, n_out, out.data_ptr(),
+                                                   _stream_handle(attn.device))
+    if rc != 0:
+        raise VlcaError(rc, "varlen_causal_attn_out_residual")
+    return out
+
+
+def attention_block(x, cu_seqlens, max_seqlen: int, gamma, beta, w_qkv, b_qkv, w_out, b_out, eps: float = 1e-5,
+                    n_heads: int = 8, scale: Optional[float] = None):
+    """The layer's attention sub-block: x + Linear_out(attention(Linear_qkv(LayerNorm(x)))),
+    three library calls (LayerNorm fused into the qkv product, bias and residual into
+    the output product)."""
+    qkv = ln_qkv(x, gamma, beta, w_qkv, b_qkv, eps)
+    attn = fwd(qkv, cu_seqlens, max_seqlen, n_heads=n_heads, scale=scale)
+    return out_residual(attn, w_out, b_out, x)
 
 
 def fwd_lse(qkv, cu_seqlens, max_seqlen: int, n_heads: int = 8, head_dim: int = 64,

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvlca.so")
 SOURCES = [os.path.join(CSRC, "vlca_kernels.hip"), os.path.join(CSRC, "vlca_backward.hip"),
-           os.path.join(CSRC, "vlca_masked.hip"),
+           os.path.join(CSRC, "vlca_masked.hip"), os.path.join(CSRC, "vlca_proj.hip"),
            os.path.join(CSRC, "vlca_noalloc.hip"),
            os.path.join(CSRC, "vlca_api.cpp"), os.path.join(CSRC, "vlca_graph.cpp")]
 # The CPython call trampoline (argument marshalling for the two launch entry points).

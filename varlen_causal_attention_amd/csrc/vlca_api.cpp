@@ -344,6 +344,34 @@ int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, in
   return VLCA_OK;
 }
 
+int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta, float eps, const void* w_qkv,
+                              const void* b_qkv, int total_tokens, int d_model, int n_out, void* qkv,
+                              hipStream_t stream) {
+  if (total_tokens < 0) return VLCA_ERR_NEGATIVE_SIZE;
+  if (d_model != 512 || n_out < 128 || n_out % 128 != 0) return VLCA_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.f) return VLCA_ERR_SCALE;
+  if (total_tokens == 0) return VLCA_OK;
+  if (x == nullptr || gamma == nullptr || beta == nullptr || w_qkv == nullptr || b_qkv == nullptr || qkv == nullptr)
+    return VLCA_ERR_NULL_POINTER;
+  if (qkv == x) return VLCA_ERR_ALIAS;
+  return vlca::launch_ln_qkv(x, gamma, beta, eps, w_qkv, b_qkv, total_tokens, n_out, qkv, stream) == hipSuccess
+             ? VLCA_OK
+             : VLCA_ERR_HIP;
+}
+
+int varlen_causal_attn_out_residual(const void* attn, const void* w_out, const void* b_out, const void* residual,
+                                    int total_tokens, int d_model, int n_out, void* y, hipStream_t stream) {
+  if (total_tokens < 0) return VLCA_ERR_NEGATIVE_SIZE;
+  if (d_model != 512 || n_out < 128 || n_out % 128 != 0) return VLCA_ERR_SHAPE;
+  if (total_tokens == 0) return VLCA_OK;
+  if (attn == nullptr || w_out == nullptr || b_out == nullptr || residual == nullptr || y == nullptr)
+    return VLCA_ERR_NULL_POINTER;
+  if (y == attn) return VLCA_ERR_ALIAS;
+  return vlca::launch_out_residual(attn, w_out, b_out, residual, total_tokens, n_out, y, stream) == hipSuccess
+             ? VLCA_OK
+             : VLCA_ERR_HIP;
+}
+
 int varlen_causal_attn_bwd(const void* qkv, const void* out, const void* dout, const float* lse,
                            const int32_t* cu_seqlens, int num_users, int max_seqlen, int n_heads, int head_dim,
                            float scale, void* dqkv, hipStream_t stream) {
@@ -472,6 +500,7 @@ const char* varlen_causal_attn_strerror(int code) {
     case VLCA_ERR_SCRATCH: return "batch needs more worklist items than the no-allocation scratch holds";
     case VLCA_ERR_BUCKETS: return "bucket sizes must be positive and strictly increasing (at most 64 buckets)";
     case VLCA_ERR_MASK: return "mask out of range (group size >= 1, windows >= -1, contexts/targets need window_right 0)";
+    case VLCA_ERR_SHAPE: return "d_model must be 512 and the output width a positive multiple of 128";
     default: return "unknown error code";
   }
 }
