@@ -155,8 +155,9 @@ def summarize_profiles(root: str, config: int, mode: str = "fwd") -> None:
     $REPO the repository root and $OUT the directory given to the runs, here
     ``root``; run from /tmp with TMPDIR=/tmp), plus ``kernel_sha.txt`` (the
     kernel_source_hash of the mode the runs used) and, optionally, ``trace.log``
-    (that run's output with the bench line).  prefix: attention_kernel (forward)
-    or backward.
+    (that run's output with the bench line).  The prefix names the measured unit
+    (PROFILE_PREFIX): the forward's attention kernel, the backward call, the
+    masked kernel or the sub-block (counters: its LayerNorm + Linear_qkv product).
     """
     import workloads
 
@@ -206,6 +207,12 @@ def summarize_profiles(root: str, config: int, mode: str = "fwd") -> None:
                              f"{ATTN_KERNEL}<false, false, false>") if any(n in r["Kernel_Name"] for r in fetch_rows)]
         kernels = names[:1]
         algorithmic = w.algorithmic_bytes()
+    elif mode == "masked":
+        kernels = ["masked_attention_kernel"]
+        algorithmic = w.algorithmic_bytes()
+    elif mode == "layer":
+        kernels = ["proj_kernel<true, false>"]
+        algorithmic = ln_qkv_algorithmic_bytes(w.total_tokens)
     else:
         kernels = ["bwd_preprocess_kernel", "schedule_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
         algorithmic = backward_algorithmic_bytes(w)
@@ -285,6 +292,16 @@ def summarize_profiles(root: str, config: int, mode: str = "fwd") -> None:
                              f"{100.0 * c.get('SQ_LDS_BANK_CONFLICT', 0.0) / c['SQ_LDS_IDX_ACTIVE']:.3f}")
         with open(out_base + "_sq.txt", "w", encoding="utf-8") as f:
             f.write("\n".join(lines) + "\n")
+
+
+def ln_qkv_algorithmic_bytes(T: int) -> int:
+    """LayerNorm + Linear_qkv: x read, qkv written, W_qkv, gamma/beta and the bias read once."""
+    return T * (512 + 1536) * 2 + 1536 * 512 * 2 + 2 * 512 * 2 + 1536 * 2
+
+
+def out_residual_algorithmic_bytes(T: int) -> int:
+    """Linear_out + bias + residual: attention output and residual read, y written, W_out and bias read once."""
+    return T * (512 * 3) * 2 + 512 * 512 * 2 + 512 * 2
 
 
 def backward_algorithmic_bytes(w) -> int:
@@ -633,8 +650,8 @@ def run_layer(args, w, dev):
           f"{ms_out * 1e3:.2f} us", file=sys.stderr, flush=True)
     f_qkv = 2.0 * T * 512 * 1536
     f_out = 2.0 * T * 512 * 512
-    b_qkv = T * (512 + 1536) * 2 + 1536 * 512 * 2 + 2 * 512 * 2 + 1536 * 2  # x, qkv, weights, gamma/beta, bias
-    b_out = T * (512 * 3) * 2 + 512 * 512 * 2 + 512 * 2                      # attn, residual, y, weights, bias
+    b_qkv = ln_qkv_algorithmic_bytes(T)
+    b_out = out_residual_algorithmic_bytes(T)
     flops = f_qkv + w.causal_flops() + f_out
     value = T / (ms_block * 1e-3)
     print(json.dumps({
