@@ -178,7 +178,7 @@ int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, in
  * + b[n_out], LayerNorm(x) = (x - mean) / sqrt(var + eps) * gamma + beta over each
  * row's 512 columns (population variance), rounded to bf16 before the product.
  * n_out = 3 * n_heads * 64 gives the forward's qkv layout; a positive multiple
- * of 128.  qkv must not overlap x.
+ * of 128, at most 65536 (else VLCA_ERR_SHAPE).  qkv must not overlap x.
  */
 int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta, float eps,
                               const void* w_qkv, const void* b_qkv, int total_tokens, int d_model,
@@ -187,7 +187,7 @@ int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta
 /*
  * varlen_causal_attn_out_residual: y[T, n_out] = residual[T, n_out] +
  * attn[T, 512] w[n_out, 512]^T + b[n_out] (n_out = d_model = 512 in the layer; a
- * positive multiple of 128).  y may be residual itself (each element is read
+ * positive multiple of 128, at most 65536).  y may be residual itself (each element is read
  * before it is written, by the same thread) but not attn.
  */
 int varlen_causal_attn_out_residual(const void* attn, const void* w_out, const void* b_out,

@@ -229,12 +229,12 @@ hipError_t launch_masked_attention(const void*, const int4* items, const int32_t
 int masked_blocks_per_cu() { return g.blocks_per_cu; }
 
 hipError_t launch_ln_qkv(const void*, const void*, const void*, float, const void*, const void*, int T, int N, void*,
-                         hipStream_t stream) {
+                         int, hipStream_t stream) {
   g.launches.push_back({'l', nullptr, 0, T, N, 0, 0, -1, {0, 0, 0, nullptr, nullptr}, stream});
   return hipSuccess;
 }
 
-hipError_t launch_out_residual(const void*, const void*, const void*, const void*, int T, int N, void*,
+hipError_t launch_out_residual(const void*, const void*, const void*, const void*, int T, int N, void*, int,
                                hipStream_t stream) {
   g.launches.push_back({'o', nullptr, 0, T, N, 0, 0, -1, {0, 0, 0, nullptr, nullptr}, stream});
   return hipSuccess;

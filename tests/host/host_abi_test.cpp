@@ -292,6 +292,33 @@ static void test_masked_entry_point() {
   CHECK(g.frees == 0 && g.syncs == 0);
 }
 
+// LayerNorm + qkv product and output product with residual: shape and argument
+// errors launch nothing; a valid call launches one kernel with T and n_out.
+static void test_neighbour_entry_points() {
+  stub::reset();
+  static char x[64], gb[64], w[64], b[64], y[64];
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 256, 1536, y, nullptr) == VLCA_ERR_SHAPE);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 1500, y, nullptr) == VLCA_ERR_SHAPE);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 0, y, nullptr) == VLCA_ERR_SHAPE);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 65536 + 128, y, nullptr) == VLCA_ERR_SHAPE);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, -1.f, w, b, 10, 512, 1536, y, nullptr) == VLCA_ERR_SCALE);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, -1, 512, 1536, y, nullptr) == VLCA_ERR_NEGATIVE_SIZE);
+  CHECK(varlen_causal_attn_ln_qkv(x, nullptr, gb, 1e-5f, w, b, 10, 512, 1536, y, nullptr) == VLCA_ERR_NULL_POINTER);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 1536, x, nullptr) == VLCA_ERR_ALIAS);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 0, 512, 1536, y, nullptr) == VLCA_OK);
+  CHECK(varlen_causal_attn_out_residual(x, w, b, y, 10, 512, 640 + 64, y, nullptr) == VLCA_ERR_SHAPE);
+  CHECK(varlen_causal_attn_out_residual(x, w, b, y, 10, 512, 65536 + 128, y, nullptr) == VLCA_ERR_SHAPE);
+  CHECK(varlen_causal_attn_out_residual(x, w, b, y, 10, 512, 512, x, nullptr) == VLCA_ERR_ALIAS);
+  CHECK(varlen_causal_attn_out_residual(x, w, nullptr, y, 10, 512, 512, y, nullptr) == VLCA_ERR_NULL_POINTER);
+  CHECK(g.launches.empty());
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 65536, y, stream_id(9)) == VLCA_OK);
+  CHECK(varlen_causal_attn_out_residual(x, w, b, y, 7, 512, 512, y, stream_id(9)) == VLCA_OK);  // y = residual
+  CHECK(g.launches.size() == 2 && g.launches[0].kind == 'l' && g.launches[0].num_users == 10 &&
+        g.launches[0].max_tiles == 65536 && g.launches[1].kind == 'o' && g.launches[1].num_users == 7 &&
+        g.launches[1].stream == stream_id(9));
+  CHECK(g.allocs == 0);
+}
+
 int main() {
   setvbuf(stdout, nullptr, _IONBF, 0);
   test_argument_errors();
@@ -302,6 +329,7 @@ int main() {
   test_graph_runner();
   test_training_entry_points();
   test_masked_entry_point();
+  test_neighbour_entry_points();
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
 }

@@ -57,6 +57,30 @@ def test_ln_qkv(gpu, T):
     _close(out.cpu(), ref, mag, f"ln_qkv T={T}")
 
 
+@pytest.mark.parametrize("T,heads,offset", [(300, 2, 0.0), (1000, 10, 0.0), (129, 8, 40.0), (6823, 8, -300.0)])
+def test_ln_qkv_shapes_and_offsets(gpu, T, heads, offset):
+    """Output widths of 3 and 15 column chunks (grids whose groups hold different
+    chunk counts), and rows whose mean dominates their spread (every third row
+    shifted by `offset`: the variance is then taken as the mean square
+    deviation)."""
+    p = workloads.make_layer_params(n_heads=heads)
+    x = workloads.draw_layer_input(T, seed=T + heads)
+    if offset:
+        xf = x.float()
+        xf[::3] += offset
+        x = xf.to(torch.bfloat16)
+    g = _gpu(p)
+    say(f"[case] ln_qkv T={T} n_out={3 * heads * 64} offset={offset}")
+    out = vlca.ln_qkv(x.cuda(), g["gamma"], g["beta"], g["w_qkv"], g["b_qkv"], eps=p.eps)
+    torch.cuda.synchronize()
+    assert out.shape == (T, 3 * heads * 64)
+    f = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    ln = oracle.layer_norm(f(x), f(p.gamma), f(p.beta), p.eps)
+    ref = oracle.linear(ln, f(p.w_qkv), f(p.b_qkv))
+    mag = np.abs(ln) @ np.abs(f(p.w_qkv)).T + np.abs(f(p.b_qkv))
+    _close(out.cpu(), ref, mag, f"ln_qkv T={T} n_out={3 * heads * 64} offset={offset}")
+
+
 @pytest.mark.parametrize("T", [1, 65, 6823, 44000])
 def test_out_residual(gpu, T):
     p = workloads.make_layer_params()

@@ -348,13 +348,16 @@ int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta
                               const void* b_qkv, int total_tokens, int d_model, int n_out, void* qkv,
                               hipStream_t stream) {
   if (total_tokens < 0) return VLCA_ERR_NEGATIVE_SIZE;
-  if (d_model != 512 || n_out < 128 || n_out % 128 != 0) return VLCA_ERR_SHAPE;
+  if (d_model != 512 || n_out < 128 || n_out % 128 != 0 || n_out > vlca::kMaxProjOut) return VLCA_ERR_SHAPE;
   if (!std::isfinite(eps) || eps < 0.f) return VLCA_ERR_SCALE;
   if (total_tokens == 0) return VLCA_OK;
   if (x == nullptr || gamma == nullptr || beta == nullptr || w_qkv == nullptr || b_qkv == nullptr || qkv == nullptr)
     return VLCA_ERR_NULL_POINTER;
   if (qkv == x) return VLCA_ERR_ALIAS;
-  return vlca::launch_ln_qkv(x, gamma, beta, eps, w_qkv, b_qkv, total_tokens, n_out, qkv, stream) == hipSuccess
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  return vlca::launch_ln_qkv(x, gamma, beta, eps, w_qkv, b_qkv, total_tokens, n_out, qkv, cu_count(dev), stream) ==
+                 hipSuccess
              ? VLCA_OK
              : VLCA_ERR_HIP;
 }
@@ -362,12 +365,15 @@ int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta
 int varlen_causal_attn_out_residual(const void* attn, const void* w_out, const void* b_out, const void* residual,
                                     int total_tokens, int d_model, int n_out, void* y, hipStream_t stream) {
   if (total_tokens < 0) return VLCA_ERR_NEGATIVE_SIZE;
-  if (d_model != 512 || n_out < 128 || n_out % 128 != 0) return VLCA_ERR_SHAPE;
+  if (d_model != 512 || n_out < 128 || n_out % 128 != 0 || n_out > vlca::kMaxProjOut) return VLCA_ERR_SHAPE;
   if (total_tokens == 0) return VLCA_OK;
   if (attn == nullptr || w_out == nullptr || b_out == nullptr || residual == nullptr || y == nullptr)
     return VLCA_ERR_NULL_POINTER;
   if (y == attn) return VLCA_ERR_ALIAS;
-  return vlca::launch_out_residual(attn, w_out, b_out, residual, total_tokens, n_out, y, stream) == hipSuccess
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  return vlca::launch_out_residual(attn, w_out, b_out, residual, total_tokens, n_out, y, cu_count(dev), stream) ==
+                 hipSuccess
              ? VLCA_OK
              : VLCA_ERR_HIP;
 }

@@ -96,12 +96,14 @@ hipError_t launch_masked_attention(const void* qkv, const int4* items, const int
 int masked_blocks_per_cu();
 
 // The attention's neighbours in the packed layer (vlca_proj.hip), d_in = 512,
-// N a multiple of 128: qkv = LayerNorm(x) W_qkv^T + b_qkv, and
-// y = residual + attn W_out^T + b_out.
+// N a multiple of 128 (at most kMaxProjOut): qkv = LayerNorm(x) W_qkv^T + b_qkv,
+// and y = residual + attn W_out^T + b_out.  cus: the device's compute units
+// (sizes the grid).
+constexpr int kMaxProjOut = 65536;
 hipError_t launch_ln_qkv(const void* x, const void* gamma, const void* beta, float eps, const void* w_qkv,
-                         const void* b_qkv, int T, int N, void* qkv, hipStream_t stream);
+                         const void* b_qkv, int T, int N, void* qkv, int cus, hipStream_t stream);
 hipError_t launch_out_residual(const void* attn, const void* w_out, const void* b_out, const void* residual, int T,
-                               int N, void* y, hipStream_t stream);
+                               int N, void* y, int cus, hipStream_t stream);
 
 // Fixed-length offsets for a captured graph: out[i] = min(cu_seqlens[min(i,
 // num_users)], total) for i = 0 .. max_users (num_users <= max_users).
