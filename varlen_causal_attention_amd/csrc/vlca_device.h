@@ -188,14 +188,17 @@ struct DiagMask {  // keys up to lim (the lane's query row on the diagonal tile)
 // the tile's first half (or of the tiles so far) -- its running max is then still
 // -inf, and the rescale factor and weight offset are taken as 1 and 0 instead of
 // the NaN that -inf - (-inf) gives; without kSafe the caller guarantees that the
-// first half of the first tile holds a visible key of every query.
+// first half of the first tile holds a visible key of every query.  halves = 1
+// (wave-uniform): the tile's second 32 keys are masked for every row of the wave
+// and are skipped -- their weights would be exactly 0, so the result is the same.
 template <bool kSafe = false, typename Mask>
 __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2],
                                           const bf16x8& ones, float sl2, float rescale_thr, Acc& A,
-                                          const Mask& mask) {
+                                          const Mask& mask, int halves = 2) {
   f32x4 s[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
+    if (b >= 2 && halves < 2) break;
     const bf16x8 k0 = lds_b128(base, L.kofs[0] + 2048 * b);
     const bf16x8 k1 = lds_b128(base, L.kofs[1] + 2048 * b);
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -218,6 +221,7 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
   // no cross-lane traffic.
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
+    if (hh >= halves) break;
     const f32x4& s0 = s[2 * hh];
     const f32x4& s1 = s[2 * hh + 1];
     const float lm = vmax(vmax(vmax(vmax(s0[0], s0[1]), s0[2]), vmax(vmax(s0[3], s1[0]), s1[1])), vmax(s1[2], s1[3]));

@@ -767,31 +767,42 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
     // (qt, the last tile of the range when khi == qt + 1) needs a mask; the last
     // tile of a first part takes the unmasked step (a uniform branch: a variable
     // mask limit cost 14 VGPRs).
+    //
+    // A wave whose 16 rows all lie past the user's end (the user's last q-tile)
+    // computes nothing: it only issues its share of the copies and meets the
+    // barriers.  On the diagonal tile a wave whose last row of the user is below
+    // key 32 skips the tile's second half, which is masked for all its rows.
     const bool diag_last = !kSplit || khi == qt + 1;
+    const bool wave_on = 16 * L.wid < len - q0;  // wave-uniform
+    const int diag_halves = min(16 * L.wid + 15, lim) >= 32 ? 2 : 1;
     int j = klo;
     for (; j + 2 < khi; j += 2) {
       wait_and_barrier<0>();
       issue_tile(kStageBytes, j + 1);
-      tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+      if (wave_on) tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
       wait_and_barrier<0>();
       issue_tile(0, j + 2);
-      tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+      if (wave_on) tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
     }
     if (j + 1 < khi) {  // two tiles left: j in stage 0, the last one goes to stage 1
       wait_and_barrier<0>();
       issue_tile(kStageBytes, j + 1);
-      tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+      if (wave_on) tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
       wait_and_barrier<0>();
-      if (diag_last)
-        tile_step(st1, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g});
-      else
+      if (!wave_on) {
+      } else if (diag_last) {
+        tile_step(st1, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
+      } else {
         tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+      }
     } else {  // one tile left, in stage 0
       wait_and_barrier<0>();
-      if (diag_last)
-        tile_step(st0, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g});
-      else
+      if (!wave_on) {
+      } else if (diag_last) {
+        tile_step(st0, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
+      } else {
         tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+      }
     }
     // The claim made at the item's start is passed on; every wave read s_next
     // before this item's first barrier.
@@ -818,7 +829,7 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       merge_parts(slot0 + (1 - part) * slot_stride, part, L, sl2, A);
     }
 
-    {
+    if (wave_on) {
       // The wave's 16 output rows go through its own rows of stage 0's K half
       // (every wave is past the item's last barrier, and only this wave copies into
       // those rows, after these reads), so that each row leaves as one 128-byte
