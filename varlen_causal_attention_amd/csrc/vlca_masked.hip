@@ -35,17 +35,34 @@
 namespace vlca {
 namespace {
 
-// The three key intervals a lane's query sees, relative to a tile's first key:
-// [0, a) (context), [bl, bh] (history or window) and [cl, ch] (own candidate
-// group); empty intervals have lo > hi.
+// The key intervals a lane's query sees, relative to a tile's first key: [0, a)
+// (context), [bl, bh] (history or window) and [cl, ch] (own candidate group).
+// Each interval test is one unsigned compare of k - lo against hi - lo (an empty
+// interval has hi - lo = -1, which no k - lo reaches... as unsigned it would be
+// the largest value, so empty intervals are given lo past every key instead).
+// kCtx / kCand: whether the context / candidate interval can meet this tile for
+// some row of the item (uniform per tile); the history interval always can.
+template <bool kCtx, bool kCand>
 struct IntervalMask {
   static constexpr bool kAny = true;
-  int a, bl, bh, cl, ch, g;
+  int a, bl, bspan, cl, cspan, g;  // spans: hi - lo as unsigned
   __device__ bool operator()(int b, int r) const {
     const int k = 16 * b + 4 * g + r;
-    return k < a || (k >= bl && k <= bh) || (k >= cl && k <= ch);
+    bool v = (uint32_t)(k - bl) <= (uint32_t)bspan;
+    if constexpr (kCtx) v = v || k < a;
+    if constexpr (kCand) v = v || (uint32_t)(k - cl) <= (uint32_t)cspan;
+    return v;
   }
 };
+
+// An interval [lo, hi] of a user's keys as (start, span) for IntervalMask: an
+// empty interval starts at 1 << 20, past every key of any tile (keys are below
+// 2^18), with span 0.
+__device__ __forceinline__ void as_span(int lo, int hi, int& start, int& span) {
+  const bool empty = lo > hi;
+  start = empty ? (1 << 20) : lo;
+  span = empty ? 0 : hi - lo;
+}
 
 __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
     const uint16_t* __restrict__ qkv, const int4* __restrict__ items, const int32_t* __restrict__ count,
@@ -164,6 +181,10 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
       bh = hi_of(i);
     }
 
+    int bstart, bspan, cstart, cspan;
+    as_span(bl, bh, bstart, bspan);
+    as_span(cl, ch, cstart, cspan);
+
     const uint16_t* kg = qkv + (int64_t)start * ldq + hd + h * kHeadDim;
     const int64_t tstride = (int64_t)kTileRows * ldq;
     // Copies of key tile jj; rows past the user's end repeat its last row.
@@ -211,7 +232,7 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
       } else {
         const int k0 = k * kTileRows;
         tile_step<true>(base, L, qf, ones, sl2, rescale_thr, A,
-                        IntervalMask{a - k0, bl - k0, bh - k0, cl - k0, ch - k0, L.g});
+                        IntervalMask<true, true>{a - k0, bstart - k0, bspan, cstart - k0, cspan, L.g});
       }
     }
     if (threadIdx.x == 0) s_next = claimed;
