@@ -134,6 +134,14 @@ __device__ __forceinline__ void dkdv_step(const LDS char* base, const Lanes& L, 
   // time: block b holds queries 16 b .. 16 b + 15; lane (g, lq) gets queries
   // 16 b + 4 g + r of the wave's key lq.
   const int key = 16 * L.wid + L.lq;  // this lane's key inside the tile
+  // Visible queries of this lane's key: qlo <= q < qvalid, with qlo = key on the
+  // diagonal tile and 0 elsewhere; tested as one unsigned compare of q - qlo
+  // against the span (0 when no query is visible).  The mask is applied only on
+  // the tiles that need it (a uniform branch), and only to P: dS = P (dP - D)
+  // is then exactly 0 as well, dP - D being finite.
+  const bool masked_tile = kMask && (diag || qvalid < kTileRows);
+  const int qlo = diag ? key : 0;
+  const uint32_t qspan = (uint32_t)max(qvalid - qlo, 0);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     f32x4 s[2], dp[2];
@@ -158,15 +166,13 @@ __device__ __forceinline__ void dkdv_step(const LDS char* base, const Lanes& L, 
       const f32x4 dd = *(const LDS f32x4*)(base + 2 * kTileBytes + 4 * kTileRows + 4 * q4);
       float p[4], ds[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[half][r], sl2, -lse[r] * kLog2eF));
-        ds[r] = p[r] * (dp[half][r] - dd[r]);
-        if (kMask) {
-          const bool vis = (!diag || q4 + r >= key) && q4 + r < qvalid;
-          p[r] = vis ? p[r] : 0.f;
-          ds[r] = vis ? ds[r] : 0.f;
-        }
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[half][r], sl2, -lse[r] * kLog2eF));
+      if (masked_tile) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = (uint32_t)(q4 + r - qlo) < qspan ? p[r] : 0.f;
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ds[r] = p[r] * (dp[half][r] - dd[r]);
       // B-operand slots of this half of 32 queries: 0..3 = block 2hh, 4..7 = block 2hh + 1.
       pw[2 * half] = pack_bf16x2(p[0], p[1]);
       pw[2 * half + 1] = pack_bf16x2(p[2], p[3]);
@@ -275,10 +281,10 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
       dk[d] = f32x4{0.f, 0.f, 0.f, 0.f};
       dv[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // Query tile j sits in stage (j - kt) % 2.  One masked step serves every tile
-    // (the diagonal masks keys after the query, the last tile rows past the
-    // user's end; elsewhere nothing): a second, unmasked copy of the step, or a
-    // loop unrolled by two, took the kernel past 128 VGPRs.
+    // Query tile j sits in stage (j - kt) % 2.  One step serves every tile, its
+    // mask under a uniform branch (the diagonal masks keys after the query, the
+    // last tile rows past the user's end; elsewhere nothing): a second, unmasked
+    // copy of the step, or a loop unrolled by two, took the kernel past 128 VGPRs.
     for (int j = kt; j <= last; ++j) {
       wait_and_barrier<0>();
       if (j + 1 <= last) issue_tile(((j + 1 - kt) & 1) * kBwdStageBytes, j + 1);
