@@ -10,10 +10,11 @@
 // This is the FlashAttention-2 backward (recompute P tile by tile from the
 // log-sum-exp; the attention backward of the recsys README's FusedHSTULayer
 // listing), laid out for CDNA4:
-//  * bwd_preprocess_kernel: D for every (row, head), written as fp32 into the
-//    first 4 bytes of that row's and head's dq columns of dqkv (the dq kernel,
-//    which runs last, reads it there before overwriting those columns), so the
-//    backward needs no scratch memory;
+//  * bwd_preprocess_kernel: D for every (row, head), and the row's
+//    -log-sum-exp log2(e), written as fp32 into the first 8 bytes of that row's
+//    and head's dq columns of dqkv (the dq kernel, which runs last, reads them
+//    there before overwriting those columns), so the backward needs no scratch
+//    memory;
 //  * bwd_dkdv_kernel: one item per (user, key tile, head); the wave's 16 key
 //    rows of K and V stay in registers as MFMA B operands while the user's
 //    query tiles from the key tile to the last stream through a two-stage LDS
@@ -90,11 +91,12 @@ struct Assign {
 
 // ------------------------------------------------------------- preprocess
 
-// D[t, h] = sum_d dO[t, h, d] * O[t, h, d] (fp32) for every row t < T =
-// cu[U] (read on the device; a persistent grid strides over the (row, head)
-// pairs): eight lanes per pair, 16 bytes of dO and of O each.
+// D[t, h] = sum_d dO[t, h, d] * O[t, h, d] (fp32), and -lse[t, h] log2(e), for
+// every row t < T = cu[U] (read on the device; a persistent grid strides over
+// the (row, head) pairs): eight lanes per pair, 16 bytes of dO and of O each.
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __restrict__ o,
                                                              const uint16_t* __restrict__ dout,
+                                                             const float* __restrict__ lse,
                                                              const int32_t* __restrict__ cu, int U, int n_heads,
                                                              uint16_t* __restrict__ dqkv) {
   const int T = max(cu[U], 0);
@@ -117,14 +119,18 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __r
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);
-    if (live && part == 0) *reinterpret_cast<float*>(dqkv + t * 3 * ldo + h * kHeadDim) = acc;
+    if (live && part == 0) {
+      float* const dst = reinterpret_cast<float*>(dqkv + t * 3 * ldo + h * kHeadDim);
+      dst[0] = acc;
+      dst[1] = -lse[t * n_heads + h] * kLog2eF;
+    }
   }
 }
 
 // ------------------------------------------------------------- dK, dV
 
 // One query tile of a dK/dV item.  base: the stage (Q tile, dO tile, the query
-// rows' log-sum-exp, D).  kMask: the diagonal tile (query q sees key k iff
+// rows' -log-sum-exp log2(e), D).  kMask: the diagonal tile (query q sees key k iff
 // q >= k) and/or the user's last query tile (rows q >= qvalid do not exist).
 template <bool kMask>
 __device__ __forceinline__ void dkdv_step(const LDS char* base, const Lanes& L, const bf16x8 (&kf)[2],
@@ -162,11 +168,11 @@ __device__ __forceinline__ void dkdv_step(const LDS char* base, const Lanes& L, 
     for (int half = 0; half < 2; ++half) {
       const int b = 2 * hh + half;
       const int q4 = 16 * b + 4 * L.g;  // first of this lane's four queries in block b
-      const f32x4 lse = *(const LDS f32x4*)(base + 2 * kTileBytes + 4 * q4);
+      const f32x4 nl = *(const LDS f32x4*)(base + 2 * kTileBytes + 4 * q4);  // -lse log2(e)
       const f32x4 dd = *(const LDS f32x4*)(base + 2 * kTileBytes + 4 * kTileRows + 4 * q4);
       float p[4], ds[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[half][r], sl2, -lse[r] * kLog2eF));
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[half][r], sl2, nl[r]));
       if (masked_tile) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = (uint32_t)(q4 + r - qlo) < qspan ? p[r] : 0.f;
@@ -246,8 +252,8 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
       }
       const int r = min(L.lane, qlim);  // this lane's query row inside the tile
       const int64_t row0 = (int64_t)start + jj * kTileRows;
-      if (L.wid == 0)
-        copy_dword_to_lds(lse + row0 * n_heads + h, (uint32_t)(r * n_heads * 4), m0s + so);
+      if (L.wid == 0)  // -lse log2(e), bytes 4..7 of the row's dq columns
+        copy_dword_to_lds(dqkv + row0 * ldq + h * kHeadDim + 2, (uint32_t)(r * ldq * 2), m0s + so);
       else if (L.wid == 1)
         copy_dword_to_lds(dqkv + row0 * ldq + h * kHeadDim, (uint32_t)(r * ldq * 2), m0s + so + 256);
     };
@@ -462,7 +468,7 @@ hipError_t launch_backward(const void* qkv, const void* out, const void* dout, c
     }
   }
   hipLaunchKernelGGL(bwd_preprocess_kernel, dim3(8 * cus), dim3(256), 0, stream, static_cast<const uint16_t*>(out),
-                     static_cast<const uint16_t*>(dout), cu_seqlens, num_users, n_heads,
+                     static_cast<const uint16_t*>(dout), lse, cu_seqlens, num_users, n_heads,
                      static_cast<uint16_t*>(dqkv));
   auto grid_of = [&](int occ) {
     int64_t g = (int64_t)cus * occ;
