@@ -224,6 +224,12 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
   asg.init(n_heads);
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2048 * L.wid));
   const uint32_t m0s = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2 * kTileBytes));
+  // Unclamped copy offsets of this lane: dO rows (stride ldo; Q rows use
+  // L.cofs_g, stride ldq) and the lane's row of the per-row values (stride ldq).
+  uint32_t ocofs[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) ocofs[i] = (uint32_t)(L.crow[i] * ldo * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i])));
+  const uint32_t lane_row_ofs = (uint32_t)(L.lane * ldq * 2);
   const int nitems = *count;
   for (int round = 0;; ++round) {
     int item, h;
@@ -240,22 +246,40 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
     const uint16_t* og = dout + (int64_t)start * ldo + h * kHeadDim;
     // This wave's copies of query tile jj into the stage at M0 offset so: Q rows,
     // dO rows (rows past the user's end repeat its last row), and, from waves 0
-    // and 1, the 64 rows' log-sum-exp and D.
+    // and 1, the 64 rows' -log-sum-exp log2(e) and D.  Only the user's last
+    // query tile clamps rows; the others take the offsets formed once below.
     auto issue_tile = [&](uint32_t so, int jj) {
-      const int qlim = len - 1 - jj * kTileRows;
+      const uint16_t* const qt_g = qg + (int64_t)jj * tstride;
+      const uint16_t* const ot_g = og + (int64_t)jj * kTileRows * ldo;
+      const int64_t row0 = (int64_t)start + jj * kTileRows;
+      uint32_t qo[2], oo[2], so_row;
+      if (jj == last) {
+        const int qlim = len - 1 - jj * kTileRows;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = min(L.crow[i], qlim);
+          const uint32_t chunk = 16 * ((L.lane & 7) ^ swz(L.crow[i]));
+          qo[i] = (uint32_t)(r * ldq * 2) + chunk;
+          oo[i] = (uint32_t)(r * ldo * 2) + chunk;
+        }
+        so_row = (uint32_t)(min(L.lane, qlim) * ldq * 2);  // this lane's query row inside the tile
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          qo[i] = L.cofs_g[i];
+          oo[i] = ocofs[i];
+        }
+        so_row = lane_row_ofs;
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int r = min(L.crow[i], qlim);
-        const uint32_t chunk = 16 * ((L.lane & 7) ^ swz(L.crow[i]));
-        copy_to_lds(qg + (int64_t)jj * tstride, (uint32_t)(r * ldq * 2) + chunk, m0 + so + 1024 * i);
-        copy_to_lds(og + (int64_t)jj * kTileRows * ldo, (uint32_t)(r * ldo * 2) + chunk, m0 + so + kTileBytes + 1024 * i);
+        copy_to_lds(qt_g, qo[i], m0 + so + 1024 * i);
+        copy_to_lds(ot_g, oo[i], m0 + so + kTileBytes + 1024 * i);
       }
-      const int r = min(L.lane, qlim);  // this lane's query row inside the tile
-      const int64_t row0 = (int64_t)start + jj * kTileRows;
       if (L.wid == 0)  // -lse log2(e), bytes 4..7 of the row's dq columns
-        copy_dword_to_lds(dqkv + row0 * ldq + h * kHeadDim + 2, (uint32_t)(r * ldq * 2), m0s + so);
+        copy_dword_to_lds(dqkv + row0 * ldq + h * kHeadDim + 2, so_row, m0s + so);
       else if (L.wid == 1)
-        copy_dword_to_lds(dqkv + row0 * ldq + h * kHeadDim, (uint32_t)(r * ldq * 2), m0s + so + 256);
+        copy_dword_to_lds(dqkv + row0 * ldq + h * kHeadDim, so_row, m0s + so + 256);
     };
     // K and V rows of the wave (its 16 keys) go into its own rows of stage 1,
     // read back as B-operand fragments before stage 1 is refilled.
@@ -386,9 +410,9 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(const uint16_t* __
       const uint16_t* kt = kg + jj * tstride;
       const uint16_t* vt = kt + hd;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = jj == qt ? min(L.crow[i], lim) : L.crow[i];
-        const uint32_t o = (uint32_t)(r * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i])));
+      for (int i = 0; i < 2; ++i) {  // only the diagonal tile clamps rows
+        const uint32_t o = jj == qt ? (uint32_t)(min(L.crow[i], lim) * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i])))
+                                    : L.cofs_g[i];
         copy_to_lds(kt, o, m0 + so + 1024 * i);
         copy_to_lds(vt, o, m0 + so + kTileBytes + 1024 * i);
       }
