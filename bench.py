@@ -214,7 +214,7 @@ def summarize_profiles(root: str, config: int, mode: str = "fwd") -> None:
         kernels = ["proj_kernel<true, false>"]
         algorithmic = ln_qkv_algorithmic_bytes(w.total_tokens)
     else:
-        kernels = ["bwd_preprocess_kernel", "schedule_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+        kernels = ["bwd_prepare_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
         algorithmic = backward_algorithmic_bytes(w)
     fetch_kib = write_kib = 0.0
     per = []
@@ -670,7 +670,7 @@ def run_layer(args, w, dev):
 
 
 def run_backward(args, w, dev):
-    """One step = one varlen_causal_attn_bwd call (D preprocess, scheduler, dK/dV and
+    """One step = one varlen_causal_attn_bwd call (worklist and row pass in one kernel, dK/dV and
     dQ kernels) over the batch, with qkv, out, dout and lse resident in HBM."""
     import torch
 
@@ -726,7 +726,7 @@ def run_backward(args, w, dev):
         "tflops": flops / (ms_step * 1e-3) / 1e12,
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": roofline(flops, nbytes, ms_step * 1e-3, measured_traffic(w.name, "bwd"),
-                             "varlen_causal_attn_bwd (preprocess, scheduler, dK/dV and dQ kernels)"),
+                             "varlen_causal_attn_bwd (prepare, dK/dV and dQ kernels)"),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, dout=dout_cpu)

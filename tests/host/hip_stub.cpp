@@ -210,10 +210,16 @@ hipError_t launch_attention_fused(const void*, const int32_t*, int num_users, in
   return hipSuccess;
 }
 
-hipError_t launch_backward(const void*, const void*, const void*, const float*, const int32_t*, int num_users,
-                           const int4* items, const int32_t* count, int64_t max_items, int n_heads, float,
-                           void*, int, hipStream_t stream) {
-  g.launches.push_back({'b', items, touch(items, count), num_users, (int)max_items, n_heads, 0, -1,
+hipError_t launch_bwd_prepare(const void*, const void*, const float*, const int32_t*, int num_users, int max_tiles,
+                              int4* items, int32_t* count, int n_heads, void*, int, hipStream_t stream) {
+  g.launches.push_back({'p', items, touch(items, count), num_users, max_tiles, n_heads, 0, -1,
+                        {0, 0, 0, nullptr, nullptr}, stream});
+  return hipSuccess;
+}
+
+hipError_t launch_backward(const void*, const void*, const float*, const int4* items, const int32_t* count,
+                           int64_t max_items, int n_heads, float, void*, int, hipStream_t stream) {
+  g.launches.push_back({'b', items, touch(items, count), 0, (int)max_items, n_heads, 0, -1,
                         {0, 0, 0, nullptr, nullptr}, stream});
   return hipSuccess;
 }

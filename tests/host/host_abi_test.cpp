@@ -247,7 +247,8 @@ static void test_training_entry_points() {
   CHECK(varlen_causal_attn_fwd_lse(QKV, CU, 60, 452, 8, 64, 0.125f, OUT, nullptr, s) == VLCA_ERR_NULL_POINTER);
   CHECK(varlen_causal_attn_fwd_lse(QKV, CU, 60, 452, 8, 64, 0.125f, OUT, lse_buf, s) == VLCA_OK);
   CHECK(g.launches.size() == 1 && g.launches[0].kind == 'f');
-  // bwd: argument checks, then the scheduler and the backward over the stream's worklist.
+  // bwd: argument checks, then the first kernel (worklist and row pass) and the
+  // gradient kernels over the stream's worklist.
   auto bwd = [&](const void* out, const void* dout, const float* lse, void* dqkv, int users, int ms) {
     return varlen_causal_attn_bwd(QKV, out, dout, lse, CU, users, ms, 8, 64, 0.125f, dqkv, s);
   };
@@ -258,8 +259,9 @@ static void test_training_entry_points() {
   CHECK(bwd(OUT, dout_buf, lse_buf, dqkv_buf, 0, 452) == VLCA_OK && bwd(OUT, dout_buf, lse_buf, dqkv_buf, 60, 0) == VLCA_OK);
   g.launches.clear();
   CHECK(bwd(OUT, dout_buf, lse_buf, dqkv_buf, 60, 452) == VLCA_OK);
-  CHECK(g.launches.size() == 2 && g.launches[0].kind == 's' && g.launches[1].kind == 'b');
-  CHECK(g.launches[0].split.p <= 1 && g.launches[1].items == g.launches[0].items);
+  CHECK(g.launches.size() == 2 && g.launches[0].kind == 'p' && g.launches[1].kind == 'b');
+  CHECK(g.launches[0].max_tiles == 8 && g.launches[0].num_users == 60);  // ceil(452 / 64) q-tiles at most
+  CHECK(g.launches[1].items == g.launches[0].items);
   CHECK(g.launches[1].max_tiles == 60 * 8);  // the worklist bound passed to the kernels
   CHECK(g.frees == 0 && g.syncs == 0);
 }

@@ -393,11 +393,11 @@ int varlen_causal_attn_bwd(const void* qkv, const void* out, const void* dout, c
   rc = get_workspace(dev, stream, need, &st);
   if (rc != VLCA_OK) return rc;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
-  if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, st.items, workspace_count(&st), nullptr,
-                            vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
+  if (vlca::launch_bwd_prepare(out, dout, lse, cu_seqlens, num_users, max_tiles, st.items, workspace_count(&st),
+                                n_heads, dqkv, cu_count(dev), stream) != hipSuccess)
     return VLCA_ERR_HIP;
-  if (vlca::launch_backward(qkv, out, dout, lse, cu_seqlens, num_users, st.items, workspace_count(&st), need, n_heads,
-                            scale, dqkv, cu_count(dev), stream) != hipSuccess)
+  if (vlca::launch_backward(qkv, dout, lse, st.items, workspace_count(&st), need, n_heads, scale, dqkv, cu_count(dev),
+                            stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;
 }

@@ -10,11 +10,11 @@
 // This is the FlashAttention-2 backward (recompute P tile by tile from the
 // log-sum-exp; the attention backward of the recsys README's FusedHSTULayer
 // listing), laid out for CDNA4:
-//  * bwd_preprocess_kernel: D for every (row, head), and the row's
-//    -log-sum-exp log2(e), written as fp32 into the first 8 bytes of that row's
-//    and head's dq columns of dqkv (the dq kernel, which runs last, reads them
-//    there before overwriting those columns), so the backward needs no scratch
-//    memory;
+//  * bwd_prepare_kernel (vlca_kernels.hip, run first, with the worklist): D
+//    for every (row, head), and the row's -log-sum-exp log2(e), written as
+//    fp32 into the first 8 bytes of that row's and head's dq columns of dqkv
+//    (the dq kernel, which runs last, reads them there before overwriting
+//    those columns), so the backward needs no scratch memory;
 //  * bwd_dkdv_kernel: one item per (user, key tile, head); the wave's 16 key
 //    rows of K and V stay in registers as MFMA B operands while the user's
 //    query tiles from the key tile to the last stream through a two-stage LDS
@@ -88,44 +88,6 @@ struct Assign {
     }
   }
 };
-
-// ------------------------------------------------------------- preprocess
-
-// D[t, h] = sum_d dO[t, h, d] * O[t, h, d] (fp32), and -lse[t, h] log2(e), for
-// every row t < T = cu[U] (read on the device; a persistent grid strides over
-// the (row, head) pairs): eight lanes per pair, 16 bytes of dO and of O each.
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(const uint16_t* __restrict__ o,
-                                                             const uint16_t* __restrict__ dout,
-                                                             const float* __restrict__ lse,
-                                                             const int32_t* __restrict__ cu, int U, int n_heads,
-                                                             uint16_t* __restrict__ dqkv) {
-  const int T = max(cu[U], 0);
-  const int64_t pairs = (int64_t)T * n_heads;
-  const int part = threadIdx.x & 7;
-  const int64_t ldo = (int64_t)n_heads * kHeadDim;
-  for (int64_t p0 = (int64_t)blockIdx.x * 32; p0 < pairs; p0 += (int64_t)gridDim.x * 32) {
-    const int64_t pair = p0 + (threadIdx.x >> 3);
-    const bool live = pair < pairs;
-    const int64_t t = live ? pair / n_heads : 0;
-    const int h = live ? (int)(pair - t * n_heads) : 0;
-    float acc = 0.f;
-    if (live) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(o + t * ldo + h * kHeadDim + 8 * part);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(dout + t * ldo + h * kHeadDim + 8 * part);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)av[i], (float)bv[i], acc);
-    }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    if (live && part == 0) {
-      float* const dst = reinterpret_cast<float*>(dqkv + t * 3 * ldo + h * kHeadDim);
-      dst[0] = acc;
-      dst[1] = -lse[t * n_heads + h] * kLog2eF;
-    }
-  }
-}
 
 // ------------------------------------------------------------- dK, dV
 
@@ -480,9 +442,9 @@ int occupancy(const void* kernel) {
 
 }  // namespace
 
-hipError_t launch_backward(const void* qkv, const void* out, const void* dout, const float* lse,
-                           const int32_t* cu_seqlens, int num_users, const int4* items, const int32_t* count,
-                           int64_t max_items, int n_heads, float scale, void* dqkv, int cus, hipStream_t stream) {
+hipError_t launch_backward(const void* qkv, const void* dout, const float* lse, const int4* items,
+                           const int32_t* count, int64_t max_items, int n_heads, float scale, void* dqkv, int cus,
+                           hipStream_t stream) {
   static int occ_dkdv = 0, occ_dq = 0;
   {
     std::lock_guard<std::mutex> lk(g_occ_mu);
@@ -491,9 +453,6 @@ hipError_t launch_backward(const void* qkv, const void* out, const void* dout, c
       occ_dq = occupancy(reinterpret_cast<const void*>(bwd_dq_kernel));
     }
   }
-  hipLaunchKernelGGL(bwd_preprocess_kernel, dim3(8 * cus), dim3(256), 0, stream, static_cast<const uint16_t*>(out),
-                     static_cast<const uint16_t*>(dout), lse, cu_seqlens, num_users, n_heads,
-                     static_cast<uint16_t*>(dqkv));
   auto grid_of = [&](int occ) {
     int64_t g = (int64_t)cus * occ;
     if (g > kMaxGrid) g = kMaxGrid;

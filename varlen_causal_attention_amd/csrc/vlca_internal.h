@@ -79,12 +79,19 @@ inline bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, in
   return num_users * max_tiles * n_heads <= static_cast<int64_t>(kFusedRounds) * grid;
 }
 
-// Backward pass over the scheduler's worklist (whole items) of this batch:
-// D = rowsum(dO o O) into dqkv's dq columns, then the dK/dV kernel and the dQ
-// kernel (see vlca_backward.hip).  cus: compute units of the device.
-hipError_t launch_backward(const void* qkv, const void* out, const void* dout, const float* lse,
-                           const int32_t* cu_seqlens, int num_users, const int4* items, const int32_t* count,
-                           int64_t max_items, int n_heads, float scale, void* dqkv, int cus, hipStream_t stream);
+// The backward's first kernel (vlca_kernels.hip): the worklist of whole items
+// (as launch_schedule without splitting or work counters) and, alongside it,
+// D = rowsum(dO o O) and -lse log2(e) into dqkv's dq columns.  cus: compute
+// units of the device.
+hipError_t launch_bwd_prepare(const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
+                              int num_users, int max_tiles, int4* items, int32_t* count, int n_heads, void* dqkv,
+                              int cus, hipStream_t stream);
+
+// The rest of the backward over that worklist: the dK/dV kernel, then the dQ
+// kernel (see vlca_backward.hip).
+hipError_t launch_backward(const void* qkv, const void* dout, const float* lse, const int4* items,
+                           const int32_t* count, int64_t max_items, int n_heads, float scale, void* dqkv, int cus,
+                           hipStream_t stream);
 
 // The forward with the HSTU-style mask variants (vlca_masked.hip) over the
 // scheduler's worklist of whole items, claiming items from the zeroed counters

@@ -296,11 +296,11 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
 }
 
 // The worklist in global memory: items[slot] = (user, q_tile, row_start, length),
-// or with key-range splitting the units described at order_items.
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ cu, int U,
-                                                                 int max_tiles, int4* __restrict__ items,
-                                                                 int32_t* __restrict__ count,
-                                                                 int32_t* __restrict__ queue, SplitArgs sp) {
+// or with key-range splitting the units described at order_items.  Run by one
+// workgroup of kSchedThreads threads.
+__device__ __forceinline__ void schedule_body(const int32_t* __restrict__ cu, int U, int max_tiles,
+                                              int4* __restrict__ items, int32_t* __restrict__ count,
+                                              int32_t* __restrict__ queue, SplitArgs sp) {
   // The attention kernel's work counters start at zero; so do the split pool's
   // arrival counters (every call also leaves them zero).
   if (queue != nullptr && threadIdx.x < kQueues) queue[threadIdx.x * kQueueStride] = 0;
@@ -322,6 +322,61 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
                                items[slot] = make_int4(x, y, sg.start, sg.len);
                              });
   if (threadIdx.x == 0) *count = S->count;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ cu, int U,
+                                                                 int max_tiles, int4* __restrict__ items,
+                                                                 int32_t* __restrict__ count,
+                                                                 int32_t* __restrict__ queue, SplitArgs sp) {
+  schedule_body(cu, U, max_tiles, items, count, queue, sp);
+}
+
+// ------------------------------------------------ backward: the first kernel
+// The backward's two independent preliminaries in one launch, so that the
+// worklist's latency hides under the row pass: workgroup 0 builds the worklist
+// (schedule_body, no split, no work counters); the others form, for every row t
+// < T = cu[U] (read on the device) and head h, with eight lanes per (row, head)
+// pair and 16 bytes of dO and of O each, a persistent grid over the pairs:
+//   D[t, h] = sum_d dO[t, h, d] O[t, h, d] (fp32), and -lse[t, h] log2(e),
+// written as fp32 into the first 8 bytes of that row's and head's dq columns of
+// dqkv (the dq kernel, which runs last, reads D there before overwriting them).
+__global__ __launch_bounds__(kSchedThreads) void bwd_prepare_kernel(
+    const int32_t* __restrict__ cu, int U, int max_tiles, int4* __restrict__ items, int32_t* __restrict__ count,
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse, int n_heads,
+    uint16_t* __restrict__ dqkv) {
+  if (blockIdx.x == 0) {
+    schedule_body(cu, U, max_tiles, items, count, nullptr, SplitArgs{0, 0, 0, nullptr, nullptr});
+    return;
+  }
+  constexpr float kLog2eF = 1.4426950408889634f;
+  const int T = max(cu[U], 0);
+  const int64_t pairs = (int64_t)T * n_heads;
+  const int part = threadIdx.x & 7;
+  const int64_t ldo = (int64_t)n_heads * kHeadDim;
+  constexpr int kPairsPerPass = kSchedThreads / 8;
+  for (int64_t p0 = (int64_t)(blockIdx.x - 1) * kPairsPerPass; p0 < pairs;
+       p0 += (int64_t)(gridDim.x - 1) * kPairsPerPass) {
+    const int64_t pair = p0 + (threadIdx.x >> 3);
+    const bool live = pair < pairs;
+    const int64_t t = live ? pair / n_heads : 0;
+    const int h = live ? (int)(pair - t * n_heads) : 0;
+    float acc = 0.f;
+    if (live) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(o + t * ldo + h * kHeadDim + 8 * part);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(dout + t * ldo + h * kHeadDim + 8 * part);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)av[i], (float)bv[i], acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (live && part == 0) {
+      float* const dst = reinterpret_cast<float*>(dqkv + t * 3 * ldo + h * kHeadDim);
+      dst[0] = acc;
+      dst[1] = -lse[t * n_heads + h] * kLog2eF;
+    }
+  }
 }
 
 // ----------------------------------------------------------------- attention
@@ -910,6 +965,16 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
                            int32_t* queue, const SplitArgs& split, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens, num_users, max_tiles,
                      items, count, queue, split);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prepare(const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
+                              int num_users, int max_tiles, int4* items, int32_t* count, int n_heads, void* dqkv,
+                              int cus, hipStream_t stream) {
+  // Workgroup 0 and two row-pass workgroups of 1024 threads per CU.
+  hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + 2 * cus), dim3(kSchedThreads), 0, stream, cu_seqlens, num_users,
+                     max_tiles, items, count, static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout),
+                     lse, n_heads, static_cast<uint16_t*>(dqkv));
   return hipGetLastError();
 }
 
