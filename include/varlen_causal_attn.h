@@ -187,8 +187,8 @@ int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta
 /*
  * varlen_causal_attn_out_residual: y[T, n_out] = residual[T, n_out] +
  * attn[T, 512] w[n_out, 512]^T + b[n_out] (n_out = d_model = 512 in the layer; a
- * positive multiple of 128, at most 65536).  y may be residual itself (each element is read
- * before it is written, by the same thread) but not attn.
+ * positive multiple of 128, at most 65536).  y may be residual itself (each workgroup reads its
+ * tile of residual before it writes that tile) but not attn.
  */
 int varlen_causal_attn_out_residual(const void* attn, const void* w_out, const void* b_out,
                                     const void* residual, int total_tokens, int d_model, int n_out,

@@ -20,7 +20,8 @@
 // ring by LDS DMA (per step 128 output columns x 64 k of each half, in
 // nn.Linear's [out, in] layout); a weight fragment read from LDS feeds two
 // MFMAs.  At a chunk's end the pair hands partial sums over through LDS and
-// each wave finishes half of the chunk's columns.  The waves of half 0 issue
+// each wave finishes half of the chunk's columns; the finished rows are staged
+// row-major in LDS and leave as whole 128-byte lines.  The waves of half 0 issue
 // every weight copy and no store; the waves of half 1 issue every store and no
 // copy: a barrier only has to wait for the copies of the waves that issued
 // them, so the stores' completion never holds the ring up.  The host picks how
@@ -53,7 +54,6 @@ constexpr int kKF = kHalf / 32;                // 32-wide k fragments a wave hol
 constexpr int kHalfStageBytes = kPBN * kPBK * 2;  // 16 KB: 128 weight rows of 128 B
 constexpr int kStepBytes = 2 * kHalfStageBytes;   // both halves of one step
 constexpr int kRedBytes = 8 * 4 * 2 * 64 * 16;    // partial sums handed over: 8 waves x 8 KB
-constexpr int kHandBytes = 4 * 4 * 2 * 64 * 8;    // half 0's finished bf16 columns: 4 waves x 4 KB
 constexpr int kMaxChunksPerBlock = 16;            // bounds the block's bias slice in LDS
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -93,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void ln_proj_kernel(const uint16_t* __res
                                                            int T, int N, int chunks_per_block) {
   __shared__ __attribute__((aligned(1024))) char ring[2 * kStepBytes];
   __shared__ __attribute__((aligned(16))) char red[kRedBytes];
-  __shared__ __attribute__((aligned(16))) u32x2 hand[kHandBytes / 8];
   __shared__ __attribute__((aligned(16))) uint16_t s_bias[kMaxChunksPerBlock * kPBN];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (LDS DMA bases are scalars)
@@ -236,12 +235,16 @@ __global__ __launch_bounds__(kThreads) void ln_proj_kernel(const uint16_t* __res
   // barrier.  [rg][h][cb 0..3][rb][lane] of f32x4.
   f32x4* const red_out = reinterpret_cast<f32x4*>(red) + (rg * 2 + h) * 512;
   const f32x4* const red_in = reinterpret_cast<const f32x4*>(red) + (rg * 2 + (1 - h)) * 512;
-  u32x2* const hand_rg = hand + rg * 512;  // [cb][rb][lane]
+  // The finished bf16 rows of the row group, staged row-major in its first 8 KB
+  // of the partial-sum buffer once both waves have read their partials: 32 rows
+  // x 256 bytes, 16-byte chunk q of row r at chunk q ^ (r % 16) (conflict-free
+  // both ways), so that half 1 writes them out as whole 128-byte lines.
+  char* const stage = red + rg * 16384;
   // This wave finishes column blocks 4 h .. 4 h + 3 of a chunk: lane (g, lq) of
   // block (cb, rb) holds row m0 + 16 rb + lq, columns 128 c + 16 (4 h + cb) + 4 g.
   f32x4 acc[8][2];
-  u32x2 pend[4][2];  // half 1: its finished bf16 values awaiting their stores
-  int pend_chunk = -1;
+  u32x2 pend[4][2];  // finished bf16 values, until they are staged
+  int pend_chunk = -1, staged_chunk = -1;
   auto finish = [&](int c) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -254,32 +257,41 @@ __global__ __launch_bounds__(kThreads) void ln_proj_kernel(const uint16_t* __res
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = h == 0 ? mine[e] + o[e] : o[e] + mine[e];
-        const u32x2 pk = {pack_bf16x2(v[0] + lo_f32(bw[0]), v[1] + hi_f32(bw[0])),
-                          pack_bf16x2(v[2] + lo_f32(bw[1]), v[3] + hi_f32(bw[1]))};
-        if (h == 0)
-          hand_rg[(cb * 2 + rb) * 64 + lane] = pk;
-        else
-          pend[cb][rb] = pk;
+        pend[cb][rb] = u32x2{pack_bf16x2(v[0] + lo_f32(bw[0]), v[1] + hi_f32(bw[0])),
+                             pack_bf16x2(v[2] + lo_f32(bw[1]), v[3] + hi_f32(bw[1]))};
       }
     }
     pend_chunk = c;
   };
-  // Half 1 stores both halves of the finished chunk (half 0's from LDS).
-  auto store_pending = [&]() {
-    if (h != 0) {
+  // Both waves of the row group stage their finished columns (after the barrier
+  // that follows the partial-sum reads).
+  auto stage_pending = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const int row = m0 + 16 * rb + lq;
-        if (row >= T) continue;
-        uint16_t* const orow = out + (int64_t)row * N + pend_chunk * kPBN + 4 * g;
+        const int r = 16 * rb + lq;
+        const int byte = 128 * h + 32 * cb + 8 * g;  // inside the row's 256 bytes
+        *(LDS u32x2*)(stage + r * 256 + ((((byte >> 4) ^ (r & 15)) << 4) | (byte & 15))) = pend[cb][rb];
+      }
+    staged_chunk = pend_chunk;
+    pend_chunk = -1;
+  };
+  // Half 1 writes the staged rows out: per instruction four rows of 256 bytes,
+  // 16 bytes a lane, non-temporal (the product's output is not read back here).
+  auto store_staged = [&]() {
+    if (h != 0) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          *reinterpret_cast<u32x2*>(orow + 16 * cb) = hand_rg[(cb * 2 + rb) * 64 + lane];
-          *reinterpret_cast<u32x2*>(orow + 16 * (4 + cb)) = pend[cb][rb];
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4), q = lane & 15;
+        const u32x4 v = *(const LDS u32x4*)(stage + r * 256 + ((q ^ (r & 15)) << 4));
+        const int row = m0 + r;
+        if (row < T)
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<u32x4*>(out + (int64_t)row * N + staged_chunk * kPBN + 8 * q));
       }
     }
-    pend_chunk = -1;
+    staged_chunk = -1;
   };
 
   int slot = 0;
@@ -287,12 +299,13 @@ __global__ __launch_bounds__(kThreads) void ln_proj_kernel(const uint16_t* __res
   for (int c = c_begin; c < c_end; ++c) {
 #pragma unroll
     for (int j = 0; j < kStepsPerChunk; ++j) {
-      // Step (c, j) landed for every wave; the other slot is free; partial sums
-      // of the previous chunk (j == 0), or half 0's finished values (j == 1),
-      // are in LDS.
+      // Step (c, j) landed for every wave; the other slot is free; the previous
+      // chunk's partial sums (j == 0) or staged rows (j == 2) are in LDS, and
+      // at j == 1 every wave is past its partial-sum reads.
       step_barrier();
       if (j == 0 && c > c_begin) finish(c - 1);
-      if (j == 1 && pend_chunk >= 0) store_pending();
+      if (j == 1 && pend_chunk >= 0) stage_pending();
+      if (j == 2 && staged_chunk >= 0) store_staged();
       if (j + 1 < kStepsPerChunk)
         issue_step(slot ^ 1, c, j + 1);
       else if (c + 1 < c_end)
@@ -334,10 +347,12 @@ __global__ __launch_bounds__(kThreads) void ln_proj_kernel(const uint16_t* __res
     }
   }
   step_barrier();
-  if (pend_chunk >= 0) store_pending();
+  if (staged_chunk >= 0) store_staged();  // a one-chunk run has none; a longer run stored its last but one at j == 2
   finish(c_end - 1);
-  lds_barrier();  // half 0's finished values visible
-  store_pending();
+  lds_barrier();  // every partial-sum read is done
+  stage_pending();
+  lds_barrier();  // the staged rows are visible
+  store_staged();
 }
 
 // Chunks per workgroup: the fewest workgroup-rounds x (row work + chunks), one
@@ -437,23 +452,38 @@ __global__ __launch_bounds__(256) void res_proj_kernel(const uint16_t* __restric
     }
   }
 
-  // Epilogue: + bias + residual, one rounding to bf16, 8-byte stores.  Each
-  // element of residual is read before the same lane writes it (y may alias it).
+  // Epilogue: + bias + residual, one rounding to bf16, staged row-major in the
+  // ring (64 rows x 256 bytes, 16-byte chunk q of row r at chunk q ^ (r % 16))
+  // and written out as whole 128-byte lines.  The workgroup reads its tile's
+  // residual before the barrier and writes the tile after it, so y may alias
+  // the residual.
+  lds_barrier();  // every wave is done with the ring
+  LDS char* const stage = st0;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int row = m0 + 32 * wr + 16 * rb + lq;
-    if (row >= T) continue;
+    const int r = 32 * wr + 16 * rb + lq;
+    const int row = min(m0 + r, T - 1);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int col = n0 + 64 * wc + 16 * cb + 4 * g;
-      const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + col);
-      const u32x2 rw = *reinterpret_cast<const u32x2*>(residual + (int64_t)row * N + col);
+      const int cl = 64 * wc + 16 * cb + 4 * g;  // column inside the tile
+      const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + n0 + cl);
+      const u32x2 rw = *reinterpret_cast<const u32x2*>(residual + (int64_t)row * N + n0 + cl);
       const float v0 = acc[cb][rb][0] + lo_f32(bw[0]) + lo_f32(rw[0]);
       const float v1 = acc[cb][rb][1] + hi_f32(bw[0]) + hi_f32(rw[0]);
       const float v2 = acc[cb][rb][2] + lo_f32(bw[1]) + lo_f32(rw[1]);
       const float v3 = acc[cb][rb][3] + hi_f32(bw[1]) + hi_f32(rw[1]);
-      *reinterpret_cast<u32x2*>(out + (int64_t)row * N + col) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+      const int byte = 2 * cl;
+      *(LDS u32x2*)(stage + r * 256 + ((((byte >> 4) ^ (r & 15)) << 4) | (byte & 15))) =
+          u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
     }
+  }
+  lds_barrier();  // the staged tile is visible; every residual read is done
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // four rows of 256 bytes per wave instruction
+    const int r = 16 * i + (tid >> 4), q = tid & 15;
+    const u32x4 v = *(const LDS u32x4*)(stage + r * 256 + ((q ^ (r & 15)) << 4));
+    if (m0 + r < T)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (int64_t)(m0 + r) * N + n0 + 8 * q));
   }
 }
 
