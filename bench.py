@@ -211,7 +211,7 @@ def summarize_profiles(root: str, config: int, mode: str = "fwd") -> None:
         kernels = ["masked_attention_kernel"]
         algorithmic = w.algorithmic_bytes()
     elif mode == "layer":
-        kernels = ["proj_kernel<true, false>"]
+        kernels = ["ln_proj_kernel"]
         algorithmic = ln_qkv_algorithmic_bytes(w.total_tokens)
     else:
         kernels = ["bwd_prepare_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
@@ -663,9 +663,9 @@ def run_layer(args, w, dev):
         "tflops": flops / (ms_block * 1e-3) / 1e12,
         "ln_qkv_us": ms_ln * 1e3, "out_residual_us": ms_out * 1e3,
         "roofline": roofline(f_qkv, b_qkv, ms_ln * 1e-3, measured_traffic(w.name, "layer"),
-                             "proj_kernel<true, false> (LayerNorm + Linear_qkv)"),
+                             "ln_proj_kernel (LayerNorm + Linear_qkv)"),
         "out_residual_roofline": roofline(f_out, b_out, ms_out * 1e-3, None,
-                                          "proj_kernel<false, true> (Linear_out + bias + residual)"),
+                                          "res_proj_kernel (Linear_out + bias + residual)"),
     }), flush=True)
 
 
