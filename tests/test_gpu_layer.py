@@ -81,6 +81,28 @@ def test_ln_qkv_shapes_and_offsets(gpu, T, heads, offset):
     _close(out.cpu(), ref, mag, f"ln_qkv T={T} n_out={3 * heads * 64} offset={offset}")
 
 
+def test_ln_qkv_wide_sampled(gpu):
+    """A 4096-column output over 44000 rows: the grid-fill model then gives each
+    workgroup its longest run (16 chunks, the bound of its bias slice).  Every
+    element of 1500 sampled rows, the first and the last rows is checked."""
+    T, n_out = 44000, 4096
+    p = workloads.make_layer_params()
+    rng = np.random.default_rng(11)
+    w = torch.from_numpy((rng.standard_normal((n_out, 512)) / np.sqrt(512)).astype(np.float32)).to(torch.bfloat16)
+    b = torch.from_numpy((0.1 * rng.standard_normal(n_out)).astype(np.float32)).to(torch.bfloat16)
+    x = workloads.draw_layer_input(T, seed=12)
+    say(f"[case] ln_qkv T={T} n_out={n_out} (sampled rows)")
+    out = vlca.ln_qkv(x.cuda(), p.gamma.cuda(), p.beta.cuda(), w.cuda(), b.cuda(), eps=p.eps)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([rng.choice(T, 1500, replace=False), [0, 1, T - 2, T - 1]]))
+    f = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    xs = f(x)[rows]
+    ln = oracle.layer_norm(xs, f(p.gamma), f(p.beta), p.eps)
+    ref = oracle.linear(ln, f(w), f(b))
+    mag = np.abs(ln) @ np.abs(f(w)).T + np.abs(f(b))
+    _close(out.cpu()[torch.from_numpy(rows)], ref, mag, f"ln_qkv T={T} n_out={n_out} sampled")
+
+
 @pytest.mark.parametrize("T", [1, 65, 6823, 44000])
 def test_out_residual(gpu, T):
     p = workloads.make_layer_params()
