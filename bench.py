@@ -110,6 +110,11 @@ def cpu_baseline(w, budget_s: float, dout=None):
 SQ_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32",
                "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE")
 
+# Counters of the wait pass: where the waves' cycles go (waiting on counters or
+# barriers, ready but not issued, issuing), in units of wave-cycles.
+WAIT_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                 "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")
+
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o run -- "
              "python3 {r}/bench.py --mode {m} --config {c} --steps 200 --warmup 2000 --no-cpu-baseline --cold-steps 0",
@@ -119,6 +124,8 @@ PROFILE_COMMANDS = {
              "python3 {r}/bench.py --mode {m} --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
     "sq": "rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " --output-format csv -d {out}/sq -o run -- "
           "python3 {r}/bench.py --mode {m} --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
+    "waits": "rocprofv3 --pmc " + " ".join(WAIT_COUNTERS) + " --output-format csv -d {out}/waits -o run -- "
+             "python3 {r}/bench.py --mode {m} --config {c} --steps 5 --warmup 1 --no-cpu-baseline --cold-steps 0",
     "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/copyf -o run -- "
              "python3 {r}/bench.py --calibrate-copy-mib 256 --steps 5",
     "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/copyw -o run -- "
@@ -291,6 +298,35 @@ def summarize_profiles(root: str, config: int, mode: str = "fwd") -> None:
                 lines.append(f"  lds_bank_conflict_pct: "
                              f"{100.0 * c.get('SQ_LDS_BANK_CONFLICT', 0.0) / c['SQ_LDS_IDX_ACTIVE']:.3f}")
         with open(out_base + "_sq.txt", "w", encoding="utf-8") as f:
+            f.write("\n".join(lines) + "\n")
+
+    # Wait pass: per kernel, each counter as a share of the waves' cycles.
+    wait_dir = os.path.join(root, "waits")
+    if os.path.exists(os.path.join(wait_dir, "run_counter_collection.csv")):
+        rows = _read_csv(os.path.join(wait_dir, "run_counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            k = _short_name(r["Kernel_Name"])
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        lines = [f"# rocprofv3 wait counters, {mode} workload {w.name}: per-dispatch averages",
+                 f"# command: {cmds['waits']}",
+                 "# SQ_WAIT_ANY: wave-cycles waiting on a counter (s_waitcnt) or a barrier; SQ_WAIT_INST_ANY:",
+                 "# wave-cycles ready but not issued; SQ_ACTIVE_INST_*: wave-cycles issuing.  Shares are of",
+                 "# SQ_WAVE_CYCLES (all resident waves' cycles).  mfma_busy is not in this pass (see _sq.txt).",
+                 f"kernel_source_sha256_16: {sha}"]
+        for k in sorted(acc):
+            c = {n: sum(v) / len(v) for n, v in acc[k].items()}
+            if not c.get("SQ_WAVE_CYCLES"):
+                continue
+            n = len(next(iter(acc[k].values())))
+            lines.append("")
+            lines.append(f"kernel: {k} ({n} dispatches)")
+            for name in WAIT_COUNTERS:
+                if name in c:
+                    share = "" if name in ("GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_WAVE_CYCLES") else \
+                        f"  ({100.0 * c[name] / c['SQ_WAVE_CYCLES']:.1f}% of wave-cycles)"
+                    lines.append(f"  {name}: {c[name]:.0f}{share}")
+        with open(out_base + "_waits.txt", "w", encoding="utf-8") as f:
             f.write("\n".join(lines) + "\n")
 
 
