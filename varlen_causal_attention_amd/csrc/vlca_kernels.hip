@@ -828,37 +828,48 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
     // barriers.  On the diagonal tile a wave whose last row of the user is below
     // key 32 skips the tile's second half, which is masked for all its rows.
     const bool diag_last = !kSplit || khi == qt + 1;
-    const bool wave_on = 16 * L.wid < len - q0;  // wave-uniform
+    const bool wave_on = __builtin_amdgcn_readfirstlane(16 * L.wid < len - q0);
     const int diag_halves = min(16 * L.wid + 15, lim) >= 32 ? 2 : 1;
-    int j = klo;
-    for (; j + 2 < khi; j += 2) {
-      wait_and_barrier<0>();
-      issue_tile(kStageBytes, j + 1);
-      if (wave_on) tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
-      wait_and_barrier<0>();
-      issue_tile(0, j + 2);
-      if (wave_on) tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
-    }
-    if (j + 1 < khi) {  // two tiles left: j in stage 0, the last one goes to stage 1
-      wait_and_barrier<0>();
-      issue_tile(kStageBytes, j + 1);
-      if (wave_on) tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
-      wait_and_barrier<0>();
-      if (!wave_on) {
-      } else if (diag_last) {
-        tile_step(st1, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
-      } else {
-        tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+    // The tile loop, in two copies: with the tile steps (a wave with rows of the
+    // user), and with the copies and barriers alone.  (A condition around each
+    // step inside one loop left the accumulators in different registers on the
+    // two paths, with copies back at every join.)
+    auto tiles = [&](auto compute) {
+      constexpr bool kOn = decltype(compute)::value;
+      int j = klo;
+      for (; j + 2 < khi; j += 2) {
+        wait_and_barrier<0>();
+        issue_tile(kStageBytes, j + 1);
+        if constexpr (kOn) tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+        wait_and_barrier<0>();
+        issue_tile(0, j + 2);
+        if constexpr (kOn) tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
       }
-    } else {  // one tile left, in stage 0
-      wait_and_barrier<0>();
-      if (!wave_on) {
-      } else if (diag_last) {
-        tile_step(st0, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
-      } else {
-        tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+      if (j + 1 < khi) {  // two tiles left: j in stage 0, the last one goes to stage 1
+        wait_and_barrier<0>();
+        issue_tile(kStageBytes, j + 1);
+        if constexpr (kOn) tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+        wait_and_barrier<0>();
+        if constexpr (kOn) {
+          if (diag_last)
+            tile_step(st1, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
+          else
+            tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+        }
+      } else {  // one tile left, in stage 0
+        wait_and_barrier<0>();
+        if constexpr (kOn) {
+          if (diag_last)
+            tile_step(st0, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
+          else
+            tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+        }
       }
-    }
+    };
+    if (wave_on)
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
     // The claim made at the item's start is passed on; every wave read s_next
     // before this item's first barrier.
     if (dyn && threadIdx.x == 0) s_next = claimed;

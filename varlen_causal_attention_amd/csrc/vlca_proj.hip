@@ -56,7 +56,6 @@ constexpr int kStepBytes = 2 * kHalfStageBytes;   // both halves of one step
 constexpr int kRedBytes = 8 * 4 * 2 * 64 * 16;    // partial sums handed over: 8 waves x 8 KB
 constexpr int kMaxChunksPerBlock = 16;            // bounds the block's bias slice in LDS
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ __forceinline__ float lo_f32(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
