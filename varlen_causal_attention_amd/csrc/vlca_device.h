@@ -172,7 +172,8 @@ struct Acc {
 };
 
 // Masks of a tile step: which of the lane's 16 keys of a tile (key 16 b + 4 g + r
-// of lane group g) its query sees.
+// of lane group g) its query sees.  A mask with kAny also tells, wave-uniformly,
+// whether it passes every key of the tile (all()): the step then skips it.
 struct NoMask {  // every key
   static constexpr bool kAny = false;
   __device__ bool operator()(int, int) const { return true; }
@@ -180,6 +181,7 @@ struct NoMask {  // every key
 struct DiagMask {  // keys up to lim (the lane's query row on the diagonal tile)
   static constexpr bool kAny = true;
   int lim, g;
+  __device__ bool all() const { return false; }
   __device__ bool operator()(int b, int r) const { return 16 * b + 4 * g + r <= lim; }
 };
 
@@ -205,11 +207,13 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[b], 0, 0, 0);
   }
   if constexpr (Mask::kAny) {
+    if (!mask.all()) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (!mask(b, r)) s[b][r] = -__builtin_inff();
+        for (int r = 0; r < 4; ++r)
+          if (!mask(b, r)) s[b][r] = -__builtin_inff();
+    }
   }
   // The tile is taken in two halves of 32 keys (score blocks 2hh, 2hh+1), so the
   // second half's QK^T MFMAs run while the first half's softmax is computed.

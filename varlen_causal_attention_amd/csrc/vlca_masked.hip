@@ -46,6 +46,8 @@ template <bool kCtx, bool kCand>
 struct IntervalMask {
   static constexpr bool kAny = true;
   int a, bl, bspan, cl, cspan, g;  // spans: hi - lo as unsigned
+  bool full;                       // wave-uniform: every row of the item sees the whole tile
+  __device__ bool all() const { return full; }
   __device__ bool operator()(int b, int r) const {
     const int k = 16 * b + 4 * g + r;
     bool v = (uint32_t)(k - bl) <= (uint32_t)bspan;
@@ -227,13 +229,13 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
       if (t + 1 < ntiles) issue_tile(((t + 1) & 1) * kStageBytes, tile_of(t + 1));
       const int k = tile_of(t);
       const LDS char* base = (t & 1) ? st1 : st0;
-      if (full_tile(k)) {
-        tile_step<true>(base, L, qf, ones, sl2, rescale_thr, A, NoMask{});
-      } else {
-        const int k0 = k * kTileRows;
-        tile_step<true>(base, L, qf, ones, sl2, rescale_thr, A,
-                        IntervalMask<true, true>{a - k0, bstart - k0, bspan, cstart - k0, cspan, L.g});
-      }
+      // One step for both kinds of tile (the mask is skipped on a tile every row
+      // sees whole): two step instances left the accumulators in different
+      // registers, copied back at every join.
+      const int k0 = k * kTileRows;
+      tile_step<true>(base, L, qf, ones, sl2, rescale_thr, A,
+                      IntervalMask<true, true>{a - k0, bstart - k0, bspan, cstart - k0, cspan, L.g,
+                                               (bool)__builtin_amdgcn_readfirstlane(full_tile(k))});
     }
     if (threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring; s_next is visible
