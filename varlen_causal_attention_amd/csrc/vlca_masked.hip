@@ -189,15 +189,17 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
 
     const uint16_t* kg = qkv + (int64_t)start * ldq + hd + h * kHeadDim;
     const int64_t tstride = (int64_t)kTileRows * ldq;
-    // Copies of key tile jj; rows past the user's end repeat its last row.
+    // Copies of key tile jj; rows past the user's end repeat its last row (a
+    // tile wholly inside the user takes the precomputed offsets).
     auto issue_tile = [&](uint32_t so, int jj) {
       const uint16_t* kt = kg + jj * tstride;
       const uint16_t* vt = kt + hd;
       const int klim = len - 1 - jj * kTileRows;
+      const bool inside = klim >= kTileRows - 1;  // uniform
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const int row = min(L.crow[r], klim);
-        const uint32_t o = (uint32_t)(row * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[r])));
+        uint32_t o = L.cofs_g[r];
+        if (!inside) o = (uint32_t)(min(L.crow[r], klim) * ldq * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[r])));
         copy_to_lds(kt, o, m0 + so + 1024 * r);
         copy_to_lds(vt, o, m0 + so + kTileBytes + 1024 * r);
       }
@@ -224,18 +226,27 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
     A.l = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < 4; ++d) A.o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int t = 0; t < ntiles; ++t) {
-      wait_and_barrier<0>();
-      if (t + 1 < ntiles) issue_tile(((t + 1) & 1) * kStageBytes, tile_of(t + 1));
-      const int k = tile_of(t);
-      const LDS char* base = (t & 1) ? st1 : st0;
-      // One step for both kinds of tile (the mask is skipped on a tile every row
-      // sees whole): two step instances left the accumulators in different
-      // registers, copied back at every join.
-      const int k0 = k * kTileRows;
+    // One step for both kinds of tile (the mask is skipped on a tile every row
+    // sees whole): two step instances left the accumulators in different
+    // registers, copied back at every join.  Tile t sits in stage t % 2; the loop
+    // is unrolled by two so that each stage's LDS addresses are fixed.
+    auto step = [&](const LDS char* base, int t) {
+      const int k = tile_of(t), k0 = k * kTileRows;
       tile_step<true>(base, L, qf, ones, sl2, rescale_thr, A,
-                      IntervalMask<true, true>{a - k0, bstart - k0, bspan, cstart - k0, cspan, L.g,
-                                               (bool)__builtin_amdgcn_readfirstlane(full_tile(k))});
+                      IntervalMask<true, true>{a - k0, bstart - k0, bspan, cstart - k0, cspan, L.g, full_tile(k)});
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      wait_and_barrier<0>();
+      issue_tile(kStageBytes, tile_of(t + 1));
+      step(st0, t);
+      wait_and_barrier<0>();
+      if (t + 2 < ntiles) issue_tile(0, tile_of(t + 2));
+      step(st1, t + 1);
+    }
+    if (t < ntiles) {
+      wait_and_barrier<0>();
+      step(st0, t);
     }
     if (threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring; s_next is visible
