@@ -154,7 +154,10 @@ struct OrderScratch {
 // computed in two passes over the users (class totals, then per-class running
 // sums in chunks of kThreads users).  emit(slot, user, q_tile, segment) stores
 // one item; S.count receives the number of items.  All threads of the
-// workgroup must call this (it contains barriers).
+// workgroup must call this (it contains barriers).  The barriers order LDS
+// only: the emitted items' global stores are not waited for (a full
+// __syncthreads() would wait for their completion at every chunk; they are
+// visible to later kernels once this one has ended).
 //
 // Key-range splitting (sp.p > 1): the same rule and decision as the
 // single-kernel plan (split when the list with split items holds at most sp.upr
@@ -176,7 +179,7 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
     S->n_whole = 0;
     S->n_split = 0;
   }
-  __syncthreads();
+  lds_barrier();
   bool split = false;
   if (sp.p > 1) {  // uniform
     // Units of the split list, saturated at sp.upr + 1 (enough to decide), and
@@ -190,15 +193,15 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
       x = min(x + min(t + e, sat), sat);
       any |= e;
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      x = min(x + __shfl_xor(x, o), sat);
-      any |= __shfl_xor(any, o);
-    }
+    // Wave sums of the per-thread saturated counts (<= 64 x sat): the total is
+    // <= sp.upr exactly when the true count is.
+    x = __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63);
+    const bool wany = __ballot(any != 0) != 0;
     if (lane == 0) {
-      __atomic_fetch_add(&S->n_split, x, __ATOMIC_RELAXED);  // <= 16 waves x sat: no overflow
-      __atomic_fetch_or(&S->n_whole, any, __ATOMIC_RELAXED);
+      __atomic_fetch_add(&S->n_split, x, __ATOMIC_RELAXED);  // <= 16 waves x 64 sat: no overflow
+      if (wany) __atomic_fetch_or(&S->n_whole, 1, __ATOMIC_RELAXED);
     }
-    __syncthreads();
+    lds_barrier();
     split = S->n_whole != 0 && S->n_split <= sp.upr;
   }
   // The count a user adds to the list: its q-tiles, or both counts packed.
@@ -220,7 +223,7 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
       pending &= ~__ballot(mine);
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (wid == 0) {  // first slot of class c = tiles of all higher classes: lane l holds class 12-l
     const int v = lane < kClasses ? S->tot[kClasses - 1 - lane] : 0;
     const int incl = wave_inclusive_sum(v);
@@ -250,7 +253,7 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
       if (lane == 63) S->wsum[wid][lc] = incl;
       pending &= ~__ballot(mine);
     }
-    __syncthreads();
+    lds_barrier();
     if (t > 0 && split) {
       int both = S->base[cl] + pre;
       for (int w = 0; w < wid; ++w) both += S->wsum[w][cl];
@@ -277,7 +280,7 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
         S->long_off[k] = off;
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int nlong = S->nlong;
     for (int i = wid; i < nlong; i += kThreads / 64) {
       const int lu = S->long_u[i];
@@ -290,9 +293,9 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
       for (int w = 0; w < kThreads / 64; ++w) sum += S->wsum[w][tid];
       S->base[tid] += sum;
     }
-    __syncthreads();
+    lds_barrier();
   }
-  __syncthreads();  // S->count and every emitted item are visible to all threads
+  lds_barrier();  // S->count is visible to all threads
 }
 
 // The worklist in global memory: items[slot] = (user, q_tile, row_start, length),
@@ -314,7 +317,7 @@ __device__ __forceinline__ void schedule_body(const int32_t* __restrict__ cu, in
   if (U > 0 && max_tiles > 0 && cached) {
     for (int i = threadIdx.x; i <= U; i += kSchedThreads) s_cu[i] = cu[i];
   }
-  __syncthreads();
+  lds_barrier();
   const int total = (U > 0 && max_tiles > 0) ? (cached ? s_cu[U] : cu[U]) : 0;
   const int nusers = max_tiles > 0 ? U : 0;
   order_items<kSchedThreads>(cu, s_cu, cached, nusers, total, max_tiles, sp, S,
