@@ -74,8 +74,11 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 
 // out = LayerNorm(x) W^T + bias (gamma, beta, eps over the 512 columns of each
-// row).  Grid: x over 128-row blocks, y over groups of chunks_per_block
-// 128-column chunks (at most kMaxChunksPerBlock).
+// row).  Grid: one workgroup per (128-row block, group of chunks_per_block
+// 128-column chunks (at most kMaxChunksPerBlock)), numbered so that the groups
+// of one row block share id % 8: workgroups are dealt to the 8 XCDs round-robin,
+// so they sit on one XCD and read the block's rows of x through one L2 (with
+// the plain (x, y) grid they sat on four).  Ids past the last row block exit.
 //
 // Wave w: row group rg = w % 4 (rows m0 .. m0 + 31), k half h = w / 4 (columns
 // 256 h .. 256 h + 255 of A and W).  The two waves of a row group form partial
@@ -89,7 +92,11 @@ __global__ __launch_bounds__(kThreads) void ln_proj_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ beta, float eps,
                                                            const uint16_t* __restrict__ w,
                                                            const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-                                                           int T, int N, int chunks_per_block) {
+                                                           int T, int N, int chunks_per_block, int groups) {
+  // id = (rb / 8) * 8 groups + 8 cg + rb % 8
+  const int bid = blockIdx.x, q = bid >> 3;
+  const int row_block = (q / groups) * 8 + (bid & 7), group = q - (q / groups) * groups;
+  if (row_block * kPBM >= T) return;  // uniform: a padding workgroup
   __shared__ __attribute__((aligned(1024))) char ring[2 * kStepBytes];
   __shared__ __attribute__((aligned(16))) char red[kRedBytes];
   __shared__ __attribute__((aligned(16))) uint16_t s_bias[kMaxChunksPerBlock * kPBN];
@@ -97,8 +104,8 @@ __global__ __launch_bounds__(kThreads) void ln_proj_kernel(const uint16_t* __res
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (LDS DMA bases are scalars)
   const int rg = wid & 3, h = wid >> 2;
   const int lq = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * kPBM + kWaveRows * rg;  // this wave's first row
-  const int c_begin = blockIdx.y * chunks_per_block;
+  const int m0 = row_block * kPBM + kWaveRows * rg;  // this wave's first row
+  const int c_begin = group * chunks_per_block;
   const int c_end = min(c_begin + chunks_per_block, N / kPBN);
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ring);
 
@@ -492,10 +499,12 @@ hipError_t launch_ln_qkv(const void* x, const void* gamma, const void* beta, flo
                          const void* b_qkv, int T, int N, void* qkv, int cus, hipStream_t stream) {
   const int cpb = chunks_per_block(T, N, cus, 0.75f);
   const int groups = (N / kPBN + cpb - 1) / cpb;
-  hipLaunchKernelGGL(ln_proj_kernel, dim3((T + kPBM - 1) / kPBM, groups), dim3(kThreads), 0, stream,
+  const int64_t row_blocks = (static_cast<int64_t>(T) + kPBM - 1) / kPBM;
+  const int64_t grid = (row_blocks + 7) / 8 * 8 * groups;  // row blocks padded to a multiple of 8
+  hipLaunchKernelGGL(ln_proj_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(gamma),
                      static_cast<const uint16_t*>(beta), eps, static_cast<const uint16_t*>(w_qkv),
-                     static_cast<const uint16_t*>(b_qkv), static_cast<uint16_t*>(qkv), T, N, cpb);
+                     static_cast<const uint16_t*>(b_qkv), static_cast<uint16_t*>(qkv), T, N, cpb, groups);
   return hipGetLastError();
 }
 
