@@ -74,9 +74,19 @@ enum {
   VLCA_ERR_BUCKETS = -12,        /* runner bucket sizes not positive and increasing,
                                     or more than 64 buckets                          */
   VLCA_ERR_MASK = -13,           /* mask description out of range (see vlca_mask)    */
-  VLCA_ERR_SHAPE = -14           /* neighbour kernels: d_model != 512, or an output
+  VLCA_ERR_SHAPE = -14,          /* neighbour kernels: d_model != 512, or an output
                                     width that is not a positive multiple of 128     */
+  VLCA_ERR_ALIGN = -15           /* a pointer breaks the alignment rule below         */
 };
+
+/*
+ * Alignment.  The kernels move 16-byte chunks: every bf16 tensor (qkv, out, dout,
+ * dqkv, x, gamma, beta, the weights, residual, y, a graph runner's static
+ * buffers) and a caller's worklist items must be 16-byte aligned; the bias
+ * vectors 8-byte aligned; cu_seqlens, lse, the worklist count, num_contexts and
+ * num_targets 4-byte aligned.  Else VLCA_ERR_ALIGN, before any device work.
+ * (Allocations of hipMalloc and of torch satisfy all of them.)
+ */
 
 /*
  * Forward pass.  Runs the segment scheduler (a compact (user, q-tile) worklist:

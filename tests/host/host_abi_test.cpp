@@ -26,7 +26,7 @@ static int failures = 0;
 static hipStream_t stream_id(int i) { return reinterpret_cast<hipStream_t>(static_cast<intptr_t>(0x1000 + 16 * i)); }
 
 // Dummy device pointers: the stand-in kernels never read qkv, cu_seqlens or out.
-static char qkv_buf[64], cu_buf[64], out_buf[64];
+alignas(256) static char qkv_buf[64], cu_buf[64], out_buf[64];
 static const void* QKV = qkv_buf;
 static const int32_t* CU = reinterpret_cast<const int32_t*>(cu_buf);
 static void* OUT = out_buf;
@@ -50,8 +50,17 @@ static void test_argument_errors() {
   int64_t cap = 0;
   CHECK(varlen_causal_attn_worklist_capacity(3, 129, &cap) == VLCA_OK && cap == 9);
   CHECK(varlen_causal_attn_build_worklist(CU, 3, 129, nullptr, 9, nullptr, nullptr) == VLCA_ERR_NULL_POINTER);
-  int32_t items[4 * 8], count = 0;
+  alignas(16) int32_t items[4 * 8];
+  int32_t count = 0;
   CHECK(varlen_causal_attn_build_worklist(CU, 3, 129, items, 8, &count, nullptr) == VLCA_ERR_CAPACITY);
+  // Misaligned tensors: refused before any device work.
+  CHECK(varlen_causal_attn_fwd(qkv_buf + 2, CU, 4, 64, 8, 64, 0.125f, OUT, nullptr) == VLCA_ERR_ALIGN);
+  CHECK(varlen_causal_attn_fwd(QKV, CU, 4, 64, 8, 64, 0.125f, out_buf + 8, nullptr) == VLCA_ERR_ALIGN);
+  CHECK(varlen_causal_attn_fwd(QKV, reinterpret_cast<const int32_t*>(cu_buf + 2), 4, 64, 8, 64, 0.125f, OUT,
+                               nullptr) == VLCA_ERR_ALIGN);
+  CHECK(varlen_causal_attn_build_worklist(CU, 3, 129, items + 1, 9, &count, nullptr) == VLCA_ERR_ALIGN);
+  CHECK(varlen_causal_attn_fwd_worklist(QKV, CU, 3, 129, 8, 64, 0.125f, items + 2, 9, &count, OUT, nullptr) ==
+        VLCA_ERR_ALIGN);
   // Nothing was launched or allocated by a refused call; no-ops launch nothing.
   CHECK(fwd(0, 64, 8, nullptr) == VLCA_OK && fwd(4, 0, 8, nullptr) == VLCA_OK);
   CHECK(g.launches.empty() && g.allocs == 0);
@@ -173,7 +182,7 @@ static void test_noalloc_entry_point() {
 
 static void test_graph_runner() {
   stub::reset();
-  static char qkv_static[16], out_static[16];
+  alignas(256) static char qkv_static[32], out_static[32];
   const int32_t pages[10] = {2560, 3072, 3584, 4096, 4608, 5120, 5632, 6144, 6656, 7168};
   vlca_graph_runner* r = nullptr;
   // Argument checks before any HIP call.
@@ -187,6 +196,8 @@ static void test_graph_runner() {
   CHECK(varlen_causal_attn_runner_create(pages, 10, 20, 8, 0.125f, nullptr, out_static, 1, &r) ==
         VLCA_ERR_NULL_POINTER);
   CHECK(varlen_causal_attn_runner_create(pages, 10, 20, 8, 0.125f, qkv_static, qkv_static, 1, &r) == VLCA_ERR_ALIAS);
+  CHECK(varlen_causal_attn_runner_create(pages, 10, 20, 8, 0.125f, qkv_static + 8, out_static, 1, &r) ==
+        VLCA_ERR_ALIGN);
   CHECK(r == nullptr && g.allocs == 0 && g.launches.empty());
 
   // Pre-capture: one graph per bucket, each the forward with 20 users and
@@ -240,8 +251,8 @@ static void test_graph_runner() {
 
 static void test_training_entry_points() {
   stub::reset();
-  static float lse_buf[16];
-  static char dout_buf[16], dqkv_buf[16];
+  alignas(256) static float lse_buf[16];
+  alignas(256) static char dout_buf[32], dqkv_buf[32];
   const hipStream_t s = stream_id(11);
   // fwd_lse: same plan as fwd; lse required.
   CHECK(varlen_causal_attn_fwd_lse(QKV, CU, 60, 452, 8, 64, 0.125f, OUT, nullptr, s) == VLCA_ERR_NULL_POINTER);
@@ -256,6 +267,11 @@ static void test_training_entry_points() {
   CHECK(bwd(OUT, dout_buf, lse_buf, nullptr, 60, 452) == VLCA_ERR_NULL_POINTER);
   CHECK(bwd(OUT, dout_buf, lse_buf, dout_buf, 60, 452) == VLCA_ERR_ALIAS);
   CHECK(bwd(OUT, dout_buf, lse_buf, const_cast<void*>(QKV), 60, 452) == VLCA_ERR_ALIAS);
+  const float* lse_odd = reinterpret_cast<const float*>(reinterpret_cast<const char*>(lse_buf) + 2);
+  CHECK(bwd(OUT, dout_buf + 8, lse_buf, dqkv_buf, 60, 452) == VLCA_ERR_ALIGN);
+  CHECK(bwd(OUT, dout_buf, lse_odd, dqkv_buf, 60, 452) == VLCA_ERR_ALIGN);
+  CHECK(varlen_causal_attn_fwd_lse(QKV, CU, 60, 452, 8, 64, 0.125f, OUT, const_cast<float*>(lse_odd), s) ==
+        VLCA_ERR_ALIGN);
   CHECK(bwd(OUT, dout_buf, lse_buf, dqkv_buf, 0, 452) == VLCA_OK && bwd(OUT, dout_buf, lse_buf, dqkv_buf, 60, 0) == VLCA_OK);
   g.launches.clear();
   CHECK(bwd(OUT, dout_buf, lse_buf, dqkv_buf, 60, 452) == VLCA_OK);
@@ -269,7 +285,7 @@ static void test_training_entry_points() {
 static void test_masked_entry_point() {
   stub::reset();
   const hipStream_t s = stream_id(12);
-  static int32_t ctx[4], tgt[4];
+  alignas(16) static int32_t ctx[4], tgt[4];
   auto fm = [&](const vlca_mask* m, int users, int ms) {
     return varlen_causal_attn_fwd_masked(QKV, CU, users, ms, 8, 64, 0.125f, m, OUT, s);
   };
@@ -298,7 +314,7 @@ static void test_masked_entry_point() {
 // errors launch nothing; a valid call launches one kernel with T and n_out.
 static void test_neighbour_entry_points() {
   stub::reset();
-  static char x[64], gb[64], w[64], b[64], y[64];
+  alignas(256) static char x[64], gb[64], w[64], b[64], y[64];
   CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 256, 1536, y, nullptr) == VLCA_ERR_SHAPE);
   CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 1500, y, nullptr) == VLCA_ERR_SHAPE);
   CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 0, y, nullptr) == VLCA_ERR_SHAPE);
@@ -312,6 +328,9 @@ static void test_neighbour_entry_points() {
   CHECK(varlen_causal_attn_out_residual(x, w, b, y, 10, 512, 65536 + 128, y, nullptr) == VLCA_ERR_SHAPE);
   CHECK(varlen_causal_attn_out_residual(x, w, b, y, 10, 512, 512, x, nullptr) == VLCA_ERR_ALIAS);
   CHECK(varlen_causal_attn_out_residual(x, w, nullptr, y, 10, 512, 512, y, nullptr) == VLCA_ERR_NULL_POINTER);
+  CHECK(varlen_causal_attn_ln_qkv(x + 8, gb, gb, 1e-5f, w, b, 10, 512, 1536, y, nullptr) == VLCA_ERR_ALIGN);
+  CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b + 2, 10, 512, 1536, y, nullptr) == VLCA_ERR_ALIGN);
+  CHECK(varlen_causal_attn_out_residual(x, w, b, y + 8, 10, 512, 512, y, nullptr) == VLCA_ERR_ALIGN);
   CHECK(g.launches.empty());
   CHECK(varlen_causal_attn_ln_qkv(x, gb, gb, 1e-5f, w, b, 10, 512, 65536, y, stream_id(9)) == VLCA_OK);
   CHECK(varlen_causal_attn_out_residual(x, w, b, y, 7, 512, 512, y, stream_id(9)) == VLCA_OK);  // y = residual

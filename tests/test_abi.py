@@ -43,7 +43,7 @@ def test_header_compiles_as_c():
 def test_constants_and_strings():
     assert vlca.tile_rows() == 64
     assert vlca.strerror(0) == "success"
-    for code in range(-14, 0):
+    for code in range(-15, 0):
         assert vlca.strerror(code) != "unknown error code"
     assert vlca.strerror(-99) == "unknown error code"
 

@@ -270,6 +270,14 @@ def test_bad_shapes_raise(gpu):
         vlca.fwd(qkv.float(), cu, 40)
     with pytest.raises(vlca.VlcaError):
         vlca.fwd(qkv, cu, 40, scale=-1.0)
+    # A view two bytes into its storage: the kernels move 16-byte chunks, so the
+    # library refuses it (VLCA_ERR_ALIGN) before any device work.
+    buf = torch.empty(qkv.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    odd = buf[1:1 + qkv.numel()].view(qkv.shape)
+    odd.copy_(qkv)
+    with pytest.raises(vlca.VlcaError) as err:
+        vlca.fwd(odd, cu, 40)
+    assert err.value.code == -15
 
 
 # Rows past cu_seqlens[-1] belong to no user: fwd must leave them as they were,

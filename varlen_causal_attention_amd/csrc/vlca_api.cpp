@@ -59,6 +59,10 @@ int64_t required_capacity(int num_users, int max_seqlen) {
   return static_cast<int64_t>(num_users) * max_tiles_of(max_seqlen);
 }
 
+// Alignment of a pointer the kernels read or write in chunks of `bytes` (a null
+// pointer passes: the null checks come first where it matters).
+bool aligned(const void* p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0; }
+
 // Size and scalar checks shared by every entry point.
 int check_sizes(int num_users, int max_seqlen) {
   if (num_users < 0 || max_seqlen < 0) return VLCA_ERR_NEGATIVE_SIZE;
@@ -76,6 +80,7 @@ int check_attention_args(const void* qkv, const int32_t* cu_seqlens, int num_use
   if (!std::isfinite(scale) || !(scale > 0.f)) return VLCA_ERR_SCALE;
   if (num_users > 0 && (qkv == nullptr || cu_seqlens == nullptr || out == nullptr)) return VLCA_ERR_NULL_POINTER;
   if (qkv != nullptr && qkv == out) return VLCA_ERR_ALIAS;
+  if (!aligned(qkv, 16) || !aligned(out, 16) || !aligned(cu_seqlens, 4)) return VLCA_ERR_ALIGN;
   return VLCA_OK;
 }
 
@@ -305,6 +310,7 @@ int varlen_causal_attn_fwd(const void* qkv, const int32_t* cu_seqlens, int num_u
 int varlen_causal_attn_fwd_lse(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
                                int n_heads, int head_dim, float scale, void* out, float* lse, hipStream_t stream) {
   if (num_users > 0 && max_seqlen > 0 && lse == nullptr) return VLCA_ERR_NULL_POINTER;
+  if (!aligned(lse, 4)) return VLCA_ERR_ALIGN;
   return fwd_impl(qkv, cu_seqlens, num_users, max_seqlen, n_heads, head_dim, scale, out, lse, stream);
 }
 int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_seqlen,
@@ -314,6 +320,7 @@ int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, in
     if (mask->target_group_size < 1 || mask->window_left < -1 || mask->window_right < -1) return VLCA_ERR_MASK;
     if ((mask->num_contexts != nullptr || mask->num_targets != nullptr) && mask->window_right != 0)
       return VLCA_ERR_MASK;
+    if (!aligned(mask->num_contexts, 4) || !aligned(mask->num_targets, 4)) return VLCA_ERR_ALIGN;
   }
   const bool plain = mask == nullptr || (mask->num_contexts == nullptr && mask->num_targets == nullptr &&
                                          mask->window_left == -1 && mask->window_right == 0);
@@ -354,6 +361,9 @@ int varlen_causal_attn_ln_qkv(const void* x, const void* gamma, const void* beta
   if (x == nullptr || gamma == nullptr || beta == nullptr || w_qkv == nullptr || b_qkv == nullptr || qkv == nullptr)
     return VLCA_ERR_NULL_POINTER;
   if (qkv == x) return VLCA_ERR_ALIAS;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(beta, 16) || !aligned(w_qkv, 16) || !aligned(qkv, 16) ||
+      !aligned(b_qkv, 8))
+    return VLCA_ERR_ALIGN;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   return vlca::launch_ln_qkv(x, gamma, beta, eps, w_qkv, b_qkv, total_tokens, n_out, qkv, cu_count(dev), stream) ==
@@ -370,6 +380,8 @@ int varlen_causal_attn_out_residual(const void* attn, const void* w_out, const v
   if (attn == nullptr || w_out == nullptr || b_out == nullptr || residual == nullptr || y == nullptr)
     return VLCA_ERR_NULL_POINTER;
   if (y == attn) return VLCA_ERR_ALIAS;
+  if (!aligned(attn, 16) || !aligned(w_out, 16) || !aligned(residual, 16) || !aligned(y, 16) || !aligned(b_out, 8))
+    return VLCA_ERR_ALIGN;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
   return vlca::launch_out_residual(attn, w_out, b_out, residual, total_tokens, n_out, y, cu_count(dev), stream) ==
@@ -385,6 +397,7 @@ int varlen_causal_attn_bwd(const void* qkv, const void* out, const void* dout, c
   if (rc != VLCA_OK) return rc;
   if (num_users > 0 && (dout == nullptr || lse == nullptr || dqkv == nullptr)) return VLCA_ERR_NULL_POINTER;
   if (dqkv != nullptr && (dqkv == qkv || dqkv == out || dqkv == dout)) return VLCA_ERR_ALIAS;
+  if (!aligned(dout, 16) || !aligned(dqkv, 16) || !aligned(lse, 4)) return VLCA_ERR_ALIGN;
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
@@ -455,6 +468,7 @@ int varlen_causal_attn_build_worklist(const int32_t* cu_seqlens, int num_users, 
   if (count == nullptr || (need > 0 && items == nullptr) || (num_users > 0 && cu_seqlens == nullptr))
     return VLCA_ERR_NULL_POINTER;
   if (capacity < need) return VLCA_ERR_CAPACITY;
+  if (!aligned(items, 16) || !aligned(count, 4) || !aligned(cu_seqlens, 4)) return VLCA_ERR_ALIGN;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, reinterpret_cast<int4*>(items), count, nullptr,
                             vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
@@ -469,6 +483,7 @@ int varlen_causal_attn_fwd_worklist(const void* qkv, const int32_t* cu_seqlens, 
   if (rc != VLCA_OK) return rc;
   if (num_users > 0 && (items == nullptr || count == nullptr)) return VLCA_ERR_NULL_POINTER;
   if (num_users > 0 && capacity < required_capacity(num_users, max_seqlen)) return VLCA_ERR_CAPACITY;
+  if (!aligned(items, 16) || !aligned(count, 4)) return VLCA_ERR_ALIGN;
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   return launch_pair(qkv, cu_seqlens, num_users, max_seqlen, n_heads, scale,
                      reinterpret_cast<int4*>(const_cast<int32_t*>(items)), const_cast<int32_t*>(count), nullptr,
@@ -507,6 +522,7 @@ const char* varlen_causal_attn_strerror(int code) {
     case VLCA_ERR_BUCKETS: return "bucket sizes must be positive and strictly increasing (at most 64 buckets)";
     case VLCA_ERR_MASK: return "mask out of range (group size >= 1, windows >= -1, contexts/targets need window_right 0)";
     case VLCA_ERR_SHAPE: return "d_model must be 512 and the output width a positive multiple of 128";
+    case VLCA_ERR_ALIGN: return "bf16 tensors and worklist items must be 16-byte aligned, biases 8-byte, int32/fp32 arrays 4-byte";
     default: return "unknown error code";
   }
 }

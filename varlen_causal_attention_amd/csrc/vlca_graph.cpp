@@ -97,6 +97,8 @@ int varlen_causal_attn_runner_create(const int32_t* bucket_tokens, int n_buckets
   if (n_heads < 1 || n_heads > 65536) return VLCA_ERR_N_HEADS;
   if (!std::isfinite(scale) || !(scale > 0.f)) return VLCA_ERR_SCALE;
   if (qkv_static == out_static) return VLCA_ERR_ALIAS;
+  if ((reinterpret_cast<uintptr_t>(qkv_static) & 15) != 0 || (reinterpret_cast<uintptr_t>(out_static) & 15) != 0)
+    return VLCA_ERR_ALIGN;
 
   auto* r = new vlca_graph_runner();
   r->buckets.assign(bucket_tokens, bucket_tokens + n_buckets);
