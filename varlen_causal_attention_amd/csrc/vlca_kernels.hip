@@ -152,7 +152,8 @@ struct OrderScratch {
 //   sum of the tiles of all higher classes + sum of the tiles of the users
 //   before u in its own class,
 // computed in two passes over the users (class totals, then per-class running
-// sums in chunks of kThreads users).  emit(slot, user, q_tile, segment) stores
+// sums in chunks of kThreads users), or, when every user fits one chunk, in one
+// pass whose per-class wave scans give both.  emit(slot, user, q_tile, segment) stores
 // one item; S.count receives the number of items.  All threads of the
 // workgroup must call this (it contains barriers).  The barriers order LDS
 // only: the emitted items' global stores are not waited for (a full
@@ -208,6 +209,88 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
   auto units_of_user = [&](int t) {
     return split ? t | ((t + split_user(t, 1, sp.min_width).split) << 15) : t;
   };
+  // The items of user u (segment s) from its first slot `both` (both counts
+  // packed when splitting).  Users of more than kShortTiles tiles are left to a
+  // whole wave (S->long_u / long_off) after the next barrier.
+  auto emit_user = [&](int u, const Seg& s, int both) {
+    const int t = s.tiles;
+    if (split) {
+      const int off = both >> 15;
+      const int roff = 2 * ((both >> 15) - (both & 0x7fff));
+      const SplitUser spl = split_user(t, 1, sp.min_width);
+      for (int i = 0; i < t + spl.split; ++i) {
+        int nk, k, p;
+        unit_of(t, spl, i, nk, k, p);
+        // A split item's parts: kind 1 + k, x = split rank r0 of its first part
+        // (ranks r0, r0 + 1 < the list's units <= sp.upr, the pool's slots per head).
+        const int kind = p > 1 ? 1 + k : 0;
+        const int x = p > 1 ? roff + i - k : u;
+        emit(off + i, x, (nk - 1) | (kind << 16), s);
+      }
+    } else if (t <= kShortTiles) {
+      for (int i = 0; i < t; ++i) emit(both + i, u, t - 1 - i, s);
+    } else {
+      const int k = __atomic_fetch_add(&S->nlong, 1, __ATOMIC_RELAXED);
+      S->long_u[k] = u;
+      S->long_off[k] = both;
+    }
+  };
+  auto emit_long = [&]() {
+    const int nlong = S->nlong;
+    for (int i = wid; i < nlong; i += kThreads / 64) {
+      const int lu = S->long_u[i];
+      const int off = S->long_off[i];
+      const Seg ls = segment_of(cu, s_cu, cached, lu, total, max_tiles);
+      for (int k = lane; k < ls.tiles; k += 64) emit(off + k, lu, ls.tiles - 1 - k, ls);
+    }
+  };
+  if (nusers <= kThreads) {  // uniform
+    // One chunk: a single pass of per-class wave scans gives each user its prefix
+    // inside its wave and each wave's class sums; wave 0 turns these into
+    // per-wave offsets and class bases.
+    const int u = tid;
+    Seg s{0, 0, 0};
+    if (u < nusers) s = segment_of(cu, s_cu, cached, u, total, max_tiles);
+    const int t = s.tiles;
+    const int cl = t > 0 ? length_class(t) : -1;
+    const int val = units_of_user(t);
+    if (lane < kClasses) S->wsum[wid][lane] = 0;
+    if (tid == 0) S->nlong = 0;
+    int pre = 0;
+    unsigned long long pending = __ballot(t > 0);
+    while (pending) {
+      const int lc = __builtin_amdgcn_readlane(cl, __builtin_ctzll(pending));
+      const bool mine = cl == lc;
+      const int x = mine ? val : 0;
+      const int incl = wave_inclusive_sum(x);
+      if (mine) pre = incl - x;
+      if (lane == 63) S->wsum[wid][lc] = incl;
+      pending &= ~__ballot(mine);
+    }
+    lds_barrier();
+    if (wid == 0) {
+      // Lane l handles class 12 - l: the exclusive prefix over the waves in place,
+      // then the class bases (tiles of all higher classes).
+      int v = 0;
+      if (lane < kClasses) {
+        const int c = kClasses - 1 - lane;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+          const int x = S->wsum[w][c];
+          S->wsum[w][c] = v;
+          v += x;
+        }
+      }
+      const int incl = wave_inclusive_sum(v);
+      if (lane < kClasses) S->base[kClasses - 1 - lane] = incl - v;
+      if (lane == kClasses - 1) S->count = split ? incl >> 15 : incl;
+    }
+    lds_barrier();
+    if (t > 0) emit_user(u, s, S->base[cl] + S->wsum[wid][cl] + pre);
+    lds_barrier();
+    emit_long();
+    return;
+  }
   // Pass 1: tiles per class (one LDS atomic per class present in a wave).
   for (int u0 = 0; u0 < nusers; u0 += kThreads) {
     const int u = u0 + tid;
@@ -254,40 +337,13 @@ __device__ void order_items(const int32_t* __restrict__ cu, CachePtr s_cu, bool 
       pending &= ~__ballot(mine);
     }
     lds_barrier();
-    if (t > 0 && split) {
+    if (t > 0) {
       int both = S->base[cl] + pre;
       for (int w = 0; w < wid; ++w) both += S->wsum[w][cl];
-      const int off = both >> 15;
-      const int roff = 2 * ((both >> 15) - (both & 0x7fff));
-      const SplitUser spl = split_user(t, 1, sp.min_width);
-      for (int i = 0; i < t + spl.split; ++i) {
-        int nk, k, p;
-        unit_of(t, spl, i, nk, k, p);
-        // A split item's parts: kind 1 + k, x = split rank r0 of its first part
-        // (ranks r0, r0 + 1 < the list's units <= sp.upr, the pool's slots per head).
-        const int kind = p > 1 ? 1 + k : 0;
-        const int x = p > 1 ? roff + i - k : u;
-        emit(off + i, x, (nk - 1) | (kind << 16), s);
-      }
-    } else if (t > 0) {
-      int off = S->base[cl] + pre;
-      for (int w = 0; w < wid; ++w) off += S->wsum[w][cl];
-      if (t <= kShortTiles) {
-        for (int i = 0; i < t; ++i) emit(off + i, u, t - 1 - i, s);
-      } else {
-        const int k = __atomic_fetch_add(&S->nlong, 1, __ATOMIC_RELAXED);
-        S->long_u[k] = u;
-        S->long_off[k] = off;
-      }
+      emit_user(u, s, both);
     }
     lds_barrier();
-    const int nlong = S->nlong;
-    for (int i = wid; i < nlong; i += kThreads / 64) {
-      const int lu = S->long_u[i];
-      const int off = S->long_off[i];
-      const Seg ls = segment_of(cu, s_cu, cached, lu, total, max_tiles);
-      for (int k = lane; k < ls.tiles; k += 64) emit(off + k, lu, ls.tiles - 1 - k, ls);
-    }
+    emit_long();
     if (tid < kClasses) {
       int sum = 0;
       for (int w = 0; w < kThreads / 64; ++w) sum += S->wsum[w][tid];
