@@ -406,10 +406,12 @@ int varlen_causal_attn_bwd(const void* qkv, const void* out, const void* dout, c
   rc = get_workspace(dev, stream, need, &st);
   if (rc != VLCA_OK) return rc;
   const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
-  if (vlca::launch_bwd_prepare(out, dout, lse, cu_seqlens, num_users, max_tiles, st.items, workspace_count(&st),
-                                n_heads, dqkv, cu_count(dev), stream) != hipSuccess)
+  int32_t* const count = workspace_count(&st);
+  int32_t* const queue = count + vlca::kQueueStride;
+  if (vlca::launch_bwd_prepare(out, dout, lse, cu_seqlens, num_users, max_tiles, st.items, count, queue, n_heads, dqkv,
+                                cu_count(dev), stream) != hipSuccess)
     return VLCA_ERR_HIP;
-  if (vlca::launch_backward(qkv, dout, lse, st.items, workspace_count(&st), need, n_heads, scale, dqkv, cu_count(dev),
+  if (vlca::launch_backward(qkv, dout, lse, st.items, count, queue, need, n_heads, scale, dqkv, cu_count(dev),
                             stream) != hipSuccess)
     return VLCA_ERR_HIP;
   return VLCA_OK;

@@ -63,26 +63,43 @@ __device__ __forceinline__ void copy_dword_to_lds(const void* base, uint32_t vof
       : "memory");
 }
 
-// Work assignment shared by both gradient kernels: with the grid a multiple of
-// H, workgroup g runs head g % H (one head per XCD for H = 8) and list slot
-// g / H of each round, in a snake over the rounds.
-struct Assign {
-  int slots, slot, head0, n_heads;
-  bool by_head;
-  __device__ void init(int nh) {
+// Work assignment, in list order (longest users first, each user's items
+// together).  With the grid a multiple of H and H <= kQueues, workgroup g always
+// runs head g % H (with H = 8, the XCD it sits on) and takes slot g / H of the
+// list's first two rounds of items, in a snake (the workgroups of the longest
+// first-round items take the shortest second-round ones); later items are
+// claimed from that head's zeroed counter in global memory, so a user's items
+// run side by side where its rows are in L2.  Otherwise work unit w runs over all
+// (item, head) pairs, heads fastest, with the same two rounds and one counter.
+// Thread 0 claims the next item while the second-round and later items run and
+// hands it over through LDS at the item's last barrier.  No claim is made at the
+// kernel's start: every workgroup claiming at once serialises the atomics on the
+// counter's line, and batches of one or two rounds need none.
+struct Claim {
+  int32_t* ctr;
+  int head0, n_heads;
+  int w0, w1;  // the workgroup's work units in the first two rounds
+  int wbase;   // work unit of claim 0
+  bool per_head;
+  __device__ void init(int32_t* queue, int nh) {
     n_heads = nh;
-    by_head = gridDim.x % nh == 0;
-    slots = by_head ? gridDim.x / nh : gridDim.x;
-    slot = by_head ? blockIdx.x / nh : blockIdx.x;
-    head0 = by_head ? blockIdx.x - slot * nh : 0;
+    per_head = gridDim.x % nh == 0 && nh <= kQueues;
+    const int slots = per_head ? gridDim.x / nh : gridDim.x;
+    head0 = per_head ? blockIdx.x % nh : 0;
+    w0 = per_head ? blockIdx.x / nh : blockIdx.x;
+    w1 = 2 * slots - 1 - w0;
+    wbase = 2 * slots;
+    ctr = queue + head0 * kQueueStride;
   }
-  __device__ void work(int round, int& item, int& h) const {
-    const int pos = (round & 1) ? slots - 1 - slot : slot;
-    if (by_head) {
-      item = round * slots + pos;
+  // The work unit of the next claim.
+  __device__ int next() const {
+    return wbase + __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ void decode(int w, int& item, int& h) const {
+    if (per_head) {
+      item = w;
       h = head0;
     } else {
-      const int w = round * slots + pos;
       item = w / n_heads;
       h = w - item * n_heads;
     }
@@ -136,8 +153,14 @@ __device__ __forceinline__ void dkdv_step(const LDS char* base, const Lanes& L, 
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[half][r], sl2, nl[r]));
       if (masked_tile) {
+        // The query indices are formed here, on the masked tiles only: the lane
+        // group passes through an empty asm so that they are not hoisted out of
+        // the item loop and held in registers across it.
+        int g = L.g;
+        asm volatile("" : "+v"(g));
+        const int qm = 16 * b + 4 * g - qlo;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = (uint32_t)(q4 + r - qlo) < qspan ? p[r] : 0.f;
+        for (int r = 0; r < 4; ++r) p[r] = (uint32_t)(qm + r) < qspan ? p[r] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) ds[r] = p[r] * (dp[half][r] - dd[r]);
@@ -171,9 +194,11 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
                                                                 const uint16_t* __restrict__ dout,
                                                                 const float* __restrict__ lse,
                                                                 const int4* __restrict__ items,
-                                                                const int32_t* __restrict__ count, int n_heads,
+                                                                const int32_t* __restrict__ count,
+                                                                int32_t* __restrict__ queue, int n_heads,
                                                                 float scale, uint16_t* __restrict__ dqkv) {
   __shared__ __attribute__((aligned(1024))) char ring_lds[2 * kBwdStageBytes];
+  __shared__ int s_next;
   LDS char* const st0 = (LDS char*)ring_lds;
   LDS char* const st1 = st0 + kBwdStageBytes;
   const int64_t ldq = 3 * n_heads * kHeadDim;
@@ -182,8 +207,8 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
   const float sl2 = scale * kLog2eF;
   Lanes L;
   make_lanes(L, ldq);
-  Assign asg;
-  asg.init(n_heads);
+  Claim cl;
+  cl.init(queue, n_heads);
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2048 * L.wid));
   const uint32_t m0s = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2 * kTileBytes));
   // Unclamped copy offsets of this lane: dO rows (stride ldo; Q rows use
@@ -193,10 +218,12 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
   for (int i = 0; i < 2; ++i) ocofs[i] = (uint32_t)(L.crow[i] * ldo * 2 + 16 * ((L.lane & 7) ^ swz(L.crow[i])));
   const uint32_t lane_row_ofs = (uint32_t)(L.lane * ldq * 2);
   const int nitems = *count;
-  for (int round = 0;; ++round) {
+  int claimed = 0;
+  for (int round = 0, w = cl.w0;; ++round, w = round == 1 ? cl.w1 : __builtin_amdgcn_readfirstlane(s_next)) {
     int item, h;
-    asg.work(round, item, h);
+    cl.decode(w, item, h);
     if (item >= nitems) break;
+    if (round >= 1 && threadIdx.x == 0) claimed = cl.next();
     const int4 it = items[item];
     const int start = it.z, len = it.w;
     const int tiles = (len + kTileRows - 1) / kTileRows;
@@ -282,6 +309,9 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
       if (j + 1 <= last) issue_tile(((j + 1 - kt) & 1) * kBwdStageBytes, j + 1);
       dkdv_step<true>((j - kt) & 1 ? st1 : st0, L, kf, vf, sl2, dk, dv, j == kt, len - j * kTileRows);
     }
+    // The claim made at the item's start is passed on; every wave read s_next
+    // before this item's first barrier.
+    if (round >= 1 && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring
     const int nvalid = len - k0 - 16 * L.wid;
     uint16_t* const drow = dqkv + ((int64_t)start + k0 + 16 * L.wid) * ldq + h * kHeadDim;
@@ -343,9 +373,11 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(const uint16_t* __
                                                               const uint16_t* __restrict__ dout,
                                                               const float* __restrict__ lse,
                                                               const int4* __restrict__ items,
-                                                              const int32_t* __restrict__ count, int n_heads,
+                                                              const int32_t* __restrict__ count,
+                                                              int32_t* __restrict__ queue, int n_heads,
                                                               float scale, uint16_t* __restrict__ dqkv) {
   __shared__ __attribute__((aligned(1024))) char ring_lds[2 * kStageBytes];
+  __shared__ int s_next;
   LDS char* const st0 = (LDS char*)ring_lds;
   LDS char* const st1 = st0 + kStageBytes;
   const int64_t ldq = 3 * n_heads * kHeadDim;
@@ -354,14 +386,16 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(const uint16_t* __
   const float sl2 = scale * kLog2eF;
   Lanes L;
   make_lanes(L, ldq);
-  Assign asg;
-  asg.init(n_heads);
+  Claim cl;
+  cl.init(queue + kBwdDqQueue, n_heads);
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2048 * L.wid));
   const int nitems = *count;
-  for (int round = 0;; ++round) {
+  int claimed = 0;
+  for (int round = 0, w = cl.w0;; ++round, w = round == 1 ? cl.w1 : __builtin_amdgcn_readfirstlane(s_next)) {
     int item, h;
-    asg.work(round, item, h);
+    cl.decode(w, item, h);
     if (item >= nitems) break;
+    if (round >= 1 && threadIdx.x == 0) claimed = cl.next();
     const int4 it = items[item];
     const int qt = it.y & 0xffff, start = it.z, len = it.w;
     const int q0 = qt * kTileRows;
@@ -426,6 +460,7 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(const uint16_t* __
       wait_and_barrier<0>();
       dq_step<true>(st0, L, qf, of, sl2, nlse, dd, dq);
     }
+    if (round >= 1 && threadIdx.x == 0) s_next = claimed;  // every wave read s_next before this item's first barrier
     wait_and_barrier<0>();  // every wave is done with the ring (and has read its D)
     store_rows(st0 + 2048 * L.wid, dq, scale, dqkv + ((int64_t)start + q0 + 16 * L.wid) * ldq + h * kHeadDim, ldq,
                len - q0 - 16 * L.wid);
@@ -443,8 +478,8 @@ int occupancy(const void* kernel) {
 }  // namespace
 
 hipError_t launch_backward(const void* qkv, const void* dout, const float* lse, const int4* items,
-                           const int32_t* count, int64_t max_items, int n_heads, float scale, void* dqkv, int cus,
-                           hipStream_t stream) {
+                           const int32_t* count, int32_t* queue, int64_t max_items, int n_heads, float scale,
+                           void* dqkv, int cus, hipStream_t stream) {
   static int occ_dkdv = 0, occ_dq = 0;
   {
     std::lock_guard<std::mutex> lk(g_occ_mu);
@@ -463,10 +498,10 @@ hipError_t launch_backward(const void* qkv, const void* dout, const float* lse, 
     return (int)(g < 1 ? 1 : g);
   };
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(grid_of(occ_dkdv)), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(dout), lse, items, count,
+                     static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(dout), lse, items, count, queue,
                      n_heads, scale, static_cast<uint16_t*>(dqkv));
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid_of(occ_dq)), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(dout), lse, items, count,
+                     static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(dout), lse, items, count, queue,
                      n_heads, scale, static_cast<uint16_t*>(dqkv));
   return hipGetLastError();
 }

@@ -80,18 +80,21 @@ inline bool fused_fits(int64_t num_users, int64_t max_tiles, int64_t n_heads, in
 }
 
 // The backward's first kernel (vlca_kernels.hip): the worklist of whole items
-// (as launch_schedule without splitting or work counters) and, alongside it,
-// D = rowsum(dO o O) and -lse log2(e) into dqkv's dq columns.  cus: compute
-// units of the device.
+// (as launch_schedule without splitting) and, alongside it, D = rowsum(dO o O)
+// and -lse log2(e) into dqkv's dq columns.  It zeroes two sets of kQueues work
+// counters at queue: the dK/dV kernel's (queue[q * kQueueStride]) and the dQ
+// kernel's (kBwdDqQueue further).  cus: compute units of the device.
+constexpr int kBwdDqQueue = kQueueStride / 2;
 hipError_t launch_bwd_prepare(const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
-                              int num_users, int max_tiles, int4* items, int32_t* count, int n_heads, void* dqkv,
-                              int cus, hipStream_t stream);
+                              int num_users, int max_tiles, int4* items, int32_t* count, int32_t* queue, int n_heads,
+                              void* dqkv, int cus, hipStream_t stream);
 
 // The rest of the backward over that worklist: the dK/dV kernel, then the dQ
-// kernel (see vlca_backward.hip).
+// kernel (see vlca_backward.hip), each claiming items from its zeroed counters
+// at queue.
 hipError_t launch_backward(const void* qkv, const void* dout, const float* lse, const int4* items,
-                           const int32_t* count, int64_t max_items, int n_heads, float scale, void* dqkv, int cus,
-                           hipStream_t stream);
+                           const int32_t* count, int32_t* queue, int64_t max_items, int n_heads, float scale,
+                           void* dqkv, int cus, hipStream_t stream);
 
 // The forward with the HSTU-style mask variants (vlca_masked.hip) over the
 // scheduler's worklist of whole items, claiming items from the zeroed counters

@@ -401,9 +401,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
 // dqkv (the dq kernel, which runs last, reads D there before overwriting them).
 __global__ __launch_bounds__(kSchedThreads) void bwd_prepare_kernel(
     const int32_t* __restrict__ cu, int U, int max_tiles, int4* __restrict__ items, int32_t* __restrict__ count,
-    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse, int n_heads,
-    uint16_t* __restrict__ dqkv) {
+    int32_t* __restrict__ queue, const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, int n_heads, uint16_t* __restrict__ dqkv) {
   if (blockIdx.x == 0) {
+    // The two gradient kernels' work counters start at zero.
+    if (threadIdx.x < 2 * kQueues)
+      queue[(threadIdx.x >> 1) * kQueueStride + (threadIdx.x & 1) * kBwdDqQueue] = 0;
     schedule_body(cu, U, max_tiles, items, count, nullptr, SplitArgs{0, 0, 0, nullptr, nullptr});
     return;
   }
@@ -1039,12 +1042,12 @@ hipError_t launch_schedule(const int32_t* cu_seqlens, int num_users, int max_til
 }
 
 hipError_t launch_bwd_prepare(const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
-                              int num_users, int max_tiles, int4* items, int32_t* count, int n_heads, void* dqkv,
-                              int cus, hipStream_t stream) {
+                              int num_users, int max_tiles, int4* items, int32_t* count, int32_t* queue, int n_heads,
+                              void* dqkv, int cus, hipStream_t stream) {
   // Workgroup 0 and two row-pass workgroups of 1024 threads per CU.
   hipLaunchKernelGGL(bwd_prepare_kernel, dim3(1 + 2 * cus), dim3(kSchedThreads), 0, stream, cu_seqlens, num_users,
-                     max_tiles, items, count, static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout),
-                     lse, n_heads, static_cast<uint16_t*>(dqkv));
+                     max_tiles, items, count, queue, static_cast<const uint16_t*>(out),
+                     static_cast<const uint16_t*>(dout), lse, n_heads, static_cast<uint16_t*>(dqkv));
   return hipGetLastError();
 }
 
