@@ -181,6 +181,14 @@ int64_t touch(const int4* items, const int32_t* count) {
   b[bytes - 1] = 1;
   return bytes;
 }
+// Zero the work counters a kernel would (sets of kQueues counters kQueueStride
+// apart, `sets` of them kBwdDqQueue apart): the address sanitizer flags a
+// workspace tail too short for them.
+void zero_queue(int32_t* queue, int sets) {
+  if (queue == nullptr) return;
+  for (int q = 0; q < kQueues; ++q)
+    for (int k = 0; k < sets; ++k) queue[q * kQueueStride + k * kBwdDqQueue] = 0;
+}
 // The split pool's arrival counters must read zero when a kernel that may split starts.
 void check_counters(const SplitArgs& split) {
   if (split.p <= 1) return;
@@ -189,8 +197,9 @@ void check_counters(const SplitArgs& split) {
 }
 }  // namespace
 
-hipError_t launch_schedule(const int32_t*, int num_users, int max_tiles, int4* items, int32_t* count, int32_t*,
-                           const SplitArgs& split, hipStream_t stream) {
+hipError_t launch_schedule(const int32_t*, int num_users, int max_tiles, int4* items, int32_t* count,
+                           int32_t* queue, const SplitArgs& split, hipStream_t stream) {
+  zero_queue(queue, 1);
   g.launches.push_back({'s', items, touch(items, count), num_users, max_tiles, 0, 1, -1, split, stream});
   return hipSuccess;
 }
@@ -211,14 +220,16 @@ hipError_t launch_attention_fused(const void*, const int32_t*, int num_users, in
 }
 
 hipError_t launch_bwd_prepare(const void*, const void*, const float*, const int32_t*, int num_users, int max_tiles,
-                              int4* items, int32_t* count, int n_heads, void*, int, hipStream_t stream) {
+                              int4* items, int32_t* count, int32_t* queue, int n_heads, void*, int,
+                              hipStream_t stream) {
+  zero_queue(queue, 2);
   g.launches.push_back({'p', items, touch(items, count), num_users, max_tiles, n_heads, 0, -1,
                         {0, 0, 0, nullptr, nullptr}, stream});
   return hipSuccess;
 }
 
 hipError_t launch_backward(const void*, const void*, const float*, const int4* items, const int32_t* count,
-                           int64_t max_items, int n_heads, float, void*, int, hipStream_t stream) {
+                           int32_t*, int64_t max_items, int n_heads, float, void*, int, hipStream_t stream) {
   g.launches.push_back({'b', items, touch(items, count), 0, (int)max_items, n_heads, 0, -1,
                         {0, 0, 0, nullptr, nullptr}, stream});
   return hipSuccess;
