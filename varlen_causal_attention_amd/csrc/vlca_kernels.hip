@@ -730,24 +730,25 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
     nitems = *count;
     qt_max = nitems > 0 ? items[0].y & 0xffff : 0;  // the first unit is of a longest user's last q-tile
   }
-  // Dynamic assignment (worklist path with work counters): instead of the fixed
-  // snake, a workgroup takes the next unclaimed item from a counter in global
-  // memory, so workgroups that drew short items take more of them.  With one
-  // head per workgroup (by_head, H <= kQueues) each head has its own counter and
-  // items are taken in list order (users kept together, so later q-tiles find
-  // the user's K/V in the L2 of the XCD serving that head); otherwise one counter
-  // runs over all (item, head) pairs, heads fastest.  Thread 0 claims the next
-  // item while the current one runs; LDS passes it to all waves at the item's
-  // last barrier.
+  // Dynamic assignment (worklist path with work counters): after the first two
+  // rounds, which follow the snake (the workgroups of the longest first-round
+  // items take the shortest second-round ones), a workgroup takes the next
+  // unclaimed item from a counter in global memory, so workgroups that drew
+  // short items take more of them.  With one head per workgroup (by_head, H <=
+  // kQueues) each head has its own counter and items are taken in list order
+  // (users kept together, so later q-tiles find the user's K/V in the L2 of the
+  // XCD serving that head); otherwise the work units run over all (item, head)
+  // pairs, heads fastest, with one counter.  Thread 0 claims the next item while
+  // the second-round and later items run; LDS passes it to all waves at the
+  // item's last barrier.  No claim precedes the first items: every workgroup
+  // claiming at the kernel's start serialises the atomics on each counter's line.
   const bool dyn = !kFused && queue != nullptr;
   const bool per_head = by_head && n_heads <= kQueues;
   int32_t* const qctr = dyn ? queue + (per_head ? head0 : 0) * kQueueStride : nullptr;
+  const int nslots = per_head ? slots : G;           // work units per round
+  const int wfirst = per_head ? slot : (int)blockIdx.x;  // this workgroup's unit of round 0
   __shared__ int s_next;
   int claimed = 0;
-  if (dyn) {
-    if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();
-  }
   for (int round = 0;; ++round) {
     int qt, start, len, h;
     // Key tiles [klo, khi) of the item; a split item's part `part` of `parts`,
@@ -777,7 +778,9 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
     } else {
       int item;
       if (dyn) {
-        const int w = __builtin_amdgcn_readfirstlane(s_next);
+        const int w = round == 0   ? wfirst
+                      : round == 1 ? 2 * nslots - 1 - wfirst
+                                   : __builtin_amdgcn_readfirstlane(s_next);
         if (per_head) {
           item = w;
           h = head0;
@@ -786,7 +789,8 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
           h = w - item * n_heads;
         }
         if (item >= nitems) break;
-        if (threadIdx.x == 0) claimed = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (round >= 1 && threadIdx.x == 0)
+          claimed = 2 * nslots + __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         work_of(round, item, h);
         if (item >= nitems) break;
@@ -934,7 +938,7 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
       tiles(std::false_type{});
     // The claim made at the item's start is passed on; every wave read s_next
     // before this item's first barrier.
-    if (dyn && threadIdx.x == 0) s_next = claimed;
+    if (dyn && round >= 1 && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring before the next item refills it
 
     if (kSplit && parts > 1) {
