@@ -84,18 +84,22 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2048 * L.wid));
   const bool causal = wr == 0;
 
-  // Claimed items: with the grid a multiple of H, head g % H from counter
-  // g % H, else one counter over (item, head) pairs.
+  // Work units: with the grid a multiple of H (and H <= kQueues), head g % H,
+  // units counted per head; else units over (item, head) pairs.  The first two
+  // rounds follow the snake over the list; later items are claimed from counter
+  // g % H (or the one counter), the claim made while the second-round and later
+  // items run.  No claim precedes the first items: every workgroup claiming at
+  // the kernel's start serialises the atomics on each counter's line.
   const bool by_head = gridDim.x % n_heads == 0;
   const bool per_head = by_head && n_heads <= kQueues;
   const int head0 = by_head ? blockIdx.x % n_heads : 0;
   int32_t* const qctr = queue + (per_head ? head0 : 0) * kQueueStride;
+  const int nslots = per_head ? gridDim.x / n_heads : gridDim.x;
+  const int wfirst = per_head ? blockIdx.x / n_heads : blockIdx.x;
   const int nitems = *count;
   __shared__ int s_next;
-  if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  lds_barrier();
-  for (;;) {
-    const int w = __builtin_amdgcn_readfirstlane(s_next);
+  for (int round = 0;; ++round) {
+    const int w = round == 0 ? wfirst : round == 1 ? 2 * nslots - 1 - wfirst : __builtin_amdgcn_readfirstlane(s_next);
     int item, h;
     if (per_head) {
       item = w;
@@ -106,7 +110,8 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
     }
     if (item >= nitems) break;
     int claimed = 0;
-    if (threadIdx.x == 0) claimed = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (round >= 1 && threadIdx.x == 0)
+      claimed = 2 * nslots + __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int4 it = items[item];
     const int u = it.x, qt = it.y & 0xffff, start = it.z, len = it.w;
     const int q0 = qt * kTileRows;
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
       wait_and_barrier<0>();
       step(st0, t);
     }
-    if (threadIdx.x == 0) s_next = claimed;
+    if (round >= 1 && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring; s_next is visible
     store_rows(st0 + 2048 * L.wid, A.o, 1.0f / A.l[0],
                out + ((int64_t)start + q0 + 16 * L.wid) * ldo + h * kHeadDim, ldo, len - q0 - 16 * L.wid);
