@@ -27,12 +27,13 @@
 //    forward: the wave's 16 query rows of Q and dO in registers, key tiles 0 ..
 //    the diagonal streaming through the ring, S^T = K Q^T and dP^T = V dO^T,
 //    dQ^T += K^T dS^T.
-// No atomics: every gradient element is produced by one workgroup, so the
-// result is deterministic.
+// No atomic accumulation: every gradient element is produced by one
+// workgroup, so the result is deterministic (atomics only hand out items).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "vlca_device.h"
 #include "vlca_internal.h"
@@ -304,11 +305,21 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
     // mask under a uniform branch (the diagonal masks keys after the query, the
     // last tile rows past the user's end; elsewhere nothing): a second, unmasked
     // copy of the step, or a loop unrolled by two, took the kernel past 128 VGPRs.
-    for (int j = kt; j <= last; ++j) {
-      wait_and_barrier<0>();
-      if (j + 1 <= last) issue_tile(((j + 1 - kt) & 1) * kBwdStageBytes, j + 1);
-      dkdv_step<true>((j - kt) & 1 ? st1 : st0, L, kf, vf, sl2, dk, dv, j == kt, len - j * kTileRows);
-    }
+    // A wave whose 16 keys all lie past the user's end (on the user's last key
+    // tile) computes nothing: it issues its share of the copies and meets the
+    // barriers, in a second copy of the loop.
+    auto query_tiles = [&](auto compute) {
+      for (int j = kt; j <= last; ++j) {
+        wait_and_barrier<0>();
+        if (j + 1 <= last) issue_tile(((j + 1 - kt) & 1) * kBwdStageBytes, j + 1);
+        if constexpr (decltype(compute)::value)
+          dkdv_step<true>((j - kt) & 1 ? st1 : st0, L, kf, vf, sl2, dk, dv, j == kt, len - j * kTileRows);
+      }
+    };
+    if (__builtin_amdgcn_readfirstlane(16 * L.wid < len - k0))
+      query_tiles(std::true_type{});
+    else
+      query_tiles(std::false_type{});
     // The claim made at the item's start is passed on; every wave read s_next
     // before this item's first barrier.
     if (round >= 1 && threadIdx.x == 0) s_next = claimed;
@@ -440,26 +451,36 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(const uint16_t* __
     f32x4 dq[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) dq[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A wave whose 16 query rows all lie past the user's end (the user's last
+    // q-tile) computes nothing: it issues its share of the copies and meets the
+    // barriers, in a second copy of the loop.
     const int khi = qt + 1;
-    int j = 0;
-    for (; j + 2 < khi; j += 2) {
-      wait_and_barrier<0>();
-      issue_tile(kStageBytes, j + 1);
-      dq_step<false>(st0, L, qf, of, sl2, nlse, dd, dq);
-      wait_and_barrier<0>();
-      issue_tile(0, j + 2);
-      dq_step<false>(st1, L, qf, of, sl2, nlse, dd, dq);
-    }
-    if (j + 1 < khi) {
-      wait_and_barrier<0>();
-      issue_tile(kStageBytes, j + 1);
-      dq_step<false>(st0, L, qf, of, sl2, nlse, dd, dq);
-      wait_and_barrier<0>();
-      dq_step<true>(st1, L, qf, of, sl2, nlse, dd, dq);
-    } else {
-      wait_and_barrier<0>();
-      dq_step<true>(st0, L, qf, of, sl2, nlse, dd, dq);
-    }
+    auto tiles = [&](auto compute) {
+      constexpr bool kOn = decltype(compute)::value;
+      int j = 0;
+      for (; j + 2 < khi; j += 2) {
+        wait_and_barrier<0>();
+        issue_tile(kStageBytes, j + 1);
+        if constexpr (kOn) dq_step<false>(st0, L, qf, of, sl2, nlse, dd, dq);
+        wait_and_barrier<0>();
+        issue_tile(0, j + 2);
+        if constexpr (kOn) dq_step<false>(st1, L, qf, of, sl2, nlse, dd, dq);
+      }
+      if (j + 1 < khi) {
+        wait_and_barrier<0>();
+        issue_tile(kStageBytes, j + 1);
+        if constexpr (kOn) dq_step<false>(st0, L, qf, of, sl2, nlse, dd, dq);
+        wait_and_barrier<0>();
+        if constexpr (kOn) dq_step<true>(st1, L, qf, of, sl2, nlse, dd, dq);
+      } else {
+        wait_and_barrier<0>();
+        if constexpr (kOn) dq_step<true>(st0, L, qf, of, sl2, nlse, dd, dq);
+      }
+    };
+    if (__builtin_amdgcn_readfirstlane(16 * L.wid < len - q0))
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
     if (round >= 1 && threadIdx.x == 0) s_next = claimed;  // every wave read s_next before this item's first barrier
     wait_and_barrier<0>();  // every wave is done with the ring (and has read its D)
     store_rows(st0 + 2048 * L.wid, dq, scale, dqkv + ((int64_t)start + q0 + 16 * L.wid) * ldq + h * kHeadDim, ldq,
