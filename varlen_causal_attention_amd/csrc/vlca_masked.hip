@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "vlca_device.h"
 #include "vlca_internal.h"
 
@@ -240,19 +242,29 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
       tile_step<true>(base, L, qf, ones, sl2, rescale_thr, A,
                       IntervalMask<true, true>{a - k0, bstart - k0, bspan, cstart - k0, cspan, L.g, full_tile(k)});
     };
-    int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
-      wait_and_barrier<0>();
-      issue_tile(kStageBytes, tile_of(t + 1));
-      step(st0, t);
-      wait_and_barrier<0>();
-      if (t + 2 < ntiles) issue_tile(0, tile_of(t + 2));
-      step(st1, t + 1);
-    }
-    if (t < ntiles) {
-      wait_and_barrier<0>();
-      step(st0, t);
-    }
+    // A wave whose 16 rows all lie past the user's end (the user's last q-tile)
+    // computes nothing: it issues its share of the copies and meets the barriers,
+    // in a second copy of the loop.
+    auto tiles = [&](auto compute) {
+      constexpr bool kOn = decltype(compute)::value;
+      int t = 0;
+      for (; t + 1 < ntiles; t += 2) {
+        wait_and_barrier<0>();
+        issue_tile(kStageBytes, tile_of(t + 1));
+        if constexpr (kOn) step(st0, t);
+        wait_and_barrier<0>();
+        if (t + 2 < ntiles) issue_tile(0, tile_of(t + 2));
+        if constexpr (kOn) step(st1, t + 1);
+      }
+      if (t < ntiles) {
+        wait_and_barrier<0>();
+        if constexpr (kOn) step(st0, t);
+      }
+    };
+    if (__builtin_amdgcn_readfirstlane(16 * L.wid < len - q0))
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
     if (round >= 1 && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring; s_next is visible
     store_rows(st0 + 2048 * L.wid, A.o, 1.0f / A.l[0],
