@@ -178,11 +178,27 @@ struct NoMask {  // every key
   static constexpr bool kAny = false;
   __device__ bool operator()(int, int) const { return true; }
 };
-struct DiagMask {  // keys up to lim (the lane's query row on the diagonal tile)
-  static constexpr bool kAny = true;
-  int lim, g;
-  __device__ bool all() const { return false; }
-  __device__ bool operator()(int b, int r) const { return 16 * b + 4 * g + r <= lim; }
+// The diagonal tile as wave W sees it (its rows 16W .. 16W+15 against keys 0..63
+// of the same rows): score blocks below W are visible whole, block W up to the
+// lane's own row (key 16W + 4g + r for r <= lq - 4g), blocks above W not at all.
+// Only blocks 0..W are formed; the weights of the others are exactly 0.
+template <int W>
+struct DiagWave {
+  static constexpr bool kAny = false;
+  static constexpr int kBlocks = W + 1;  // score blocks formed
+  static constexpr int kPartial = W;     // the block masked per lane
+  int lim;                               // lq - 4g
+};
+
+// Score blocks a mask lets the step form, and the one it masks per lane (-1:
+// none); masks that do not say are taken whole (kAny decides per key).
+template <typename M, typename = void>
+struct MaskShape {
+  static constexpr int kBlocks = 4, kPartial = -1;
+};
+template <typename M>
+struct MaskShape<M, decltype((void)M::kPartial)> {
+  static constexpr int kBlocks = M::kBlocks, kPartial = M::kPartial;
 };
 
 // One key tile of one item: S^T = K Q^T, mask, softmax update, O^T += V^T P^T
@@ -197,10 +213,12 @@ template <bool kSafe = false, typename Mask>
 __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2],
                                           const bf16x8& ones, float sl2, float rescale_thr, Acc& A,
                                           const Mask& mask, int halves = 2) {
+  constexpr int kNB = MaskShape<Mask>::kBlocks;
+  constexpr int kPB = MaskShape<Mask>::kPartial;
   f32x4 s[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    if (b >= 2 && halves < 2) break;
+    if (b >= kNB || (b >= 2 && halves < 2)) break;
     const bf16x8 k0 = lds_b128(base, L.kofs[0] + 2048 * b);
     const bf16x8 k1 = lds_b128(base, L.kofs[1] + 2048 * b);
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -215,6 +233,11 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
           if (!mask(b, r)) s[b][r] = -__builtin_inff();
     }
   }
+  if constexpr (kPB >= 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r > mask.lim) s[kPB][r] = -__builtin_inff();
+  }
   // The tile is taken in two halves of 32 keys (score blocks 2hh, 2hh+1), so the
   // second half's QK^T MFMAs run while the first half's softmax is computed.
   // Lane-local max over this lane's 8 keys of the half.  The reference max m of a
@@ -222,13 +245,18 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
   // than the threshold (and on the first tile, m = -inf; the first half always
   // holds a visible key of every query) is the true max formed across the lane
   // groups and m raised, with the accumulators rescaled.  The common path needs
-  // no cross-lane traffic.
+  // no cross-lane traffic.  A block the mask leaves unformed (the half's second
+  // block) weighs 0, and its V^T fragments are taken as 0.
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    if (hh >= halves) break;
+    if (2 * hh >= kNB || hh >= halves) break;
+    const bool two = 2 * hh + 1 < kNB;  // the half's second block is formed
     const f32x4& s0 = s[2 * hh];
-    const f32x4& s1 = s[2 * hh + 1];
-    const float lm = vmax(vmax(vmax(vmax(s0[0], s0[1]), s0[2]), vmax(vmax(s0[3], s1[0]), s1[1])), vmax(s1[2], s1[3]));
+    float lm = vmax(vmax(s0[0], s0[1]), vmax(s0[2], s0[3]));
+    if (two) {
+      const f32x4& s1 = s[2 * hh + 1];
+      lm = vmax(vmax(vmax(lm, s1[0]), s1[1]), vmax(s1[2], s1[3]));
+    }
     if (__any(lm > A.mthr)) {  // wave-uniform
       const float mt = max_across_lane_groups(lm);
       const float mn = fmaxf(A.m, mt);
@@ -249,15 +277,21 @@ __device__ __forceinline__ void tile_step(const LDS char* base, const Lanes& L, 
                        __builtin_amdgcn_exp2f(__builtin_fmaf(s0[1], sl2, moff)));
     pw.y = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[2], sl2, moff)),
                        __builtin_amdgcn_exp2f(__builtin_fmaf(s0[3], sl2, moff)));
-    pw.z = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[0], sl2, moff)),
-                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[1], sl2, moff)));
-    pw.w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2], sl2, moff)),
-                       __builtin_amdgcn_exp2f(__builtin_fmaf(s1[3], sl2, moff)));
+    if (two) {
+      const f32x4& s1 = s[2 * hh + 1];
+      pw.z = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[0], sl2, moff)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(s1[1], sl2, moff)));
+      pw.w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[2], sl2, moff)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(s1[3], sl2, moff)));
+    } else {
+      pw.z = 0u;
+      pw.w = 0u;
+    }
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const bf16x4 lo = lds_tr16(base, L.vofs[d] + 4096 * hh);
-      const bf16x4 hi = lds_tr16(base, L.vofs[d] + 4096 * hh + 2048);
+      const bf16x4 hi = two ? lds_tr16(base, L.vofs[d] + 4096 * hh + 2048) : bf16x4{};
       const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       A.o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, A.o[d], 0, 0, 0);
     }

@@ -891,11 +891,25 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
     //
     // A wave whose 16 rows all lie past the user's end (the user's last q-tile)
     // computes nothing: it only issues its share of the copies and meets the
-    // barriers.  On the diagonal tile a wave whose last row of the user is below
-    // key 32 skips the tile's second half, which is masked for all its rows.
+    // barriers.
     const bool diag_last = !kSplit || khi == qt + 1;
     const bool wave_on = __builtin_amdgcn_readfirstlane(16 * L.wid < len - q0);
-    const int diag_halves = min(16 * L.wid + 15, lim) >= 32 ? 2 : 1;
+    // The diagonal tile, specialised for each wave (blocks above the wave's rows
+    // are neither formed nor weighed); it ends an item once, so its stage is a
+    // run-time choice.
+    auto last_step = [&](const LDS char* base) {
+      if (!diag_last) {
+        tile_step(base, L, qf, ones, sl2, rescale_thr, A, NoMask{});
+        return;
+      }
+      const int lim = L.lq - 4 * L.g;
+      switch (__builtin_amdgcn_readfirstlane(L.wid)) {
+        case 0: tile_step(base, L, qf, ones, sl2, rescale_thr, A, DiagWave<0>{lim}); break;
+        case 1: tile_step(base, L, qf, ones, sl2, rescale_thr, A, DiagWave<1>{lim}); break;
+        case 2: tile_step(base, L, qf, ones, sl2, rescale_thr, A, DiagWave<2>{lim}); break;
+        default: tile_step(base, L, qf, ones, sl2, rescale_thr, A, DiagWave<3>{lim}); break;
+      }
+    };
     // The tile loop, in two copies: with the tile steps (a wave with rows of the
     // user), and with the copies and barriers alone.  (A condition around each
     // step inside one loop left the accumulators in different registers on the
@@ -911,26 +925,14 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
         issue_tile(0, j + 2);
         if constexpr (kOn) tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
       }
-      if (j + 1 < khi) {  // two tiles left: j in stage 0, the last one goes to stage 1
+      const bool two_left = j + 1 < khi;  // j in stage 0, the last one goes to stage 1
+      if (two_left) {
         wait_and_barrier<0>();
         issue_tile(kStageBytes, j + 1);
         if constexpr (kOn) tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
-        wait_and_barrier<0>();
-        if constexpr (kOn) {
-          if (diag_last)
-            tile_step(st1, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
-          else
-            tile_step(st1, L, qf, ones, sl2, rescale_thr, A, NoMask{});
-        }
-      } else {  // one tile left, in stage 0
-        wait_and_barrier<0>();
-        if constexpr (kOn) {
-          if (diag_last)
-            tile_step(st0, L, qf, ones, sl2, rescale_thr, A, DiagMask{L.qr, L.g}, diag_halves);
-          else
-            tile_step(st0, L, qf, ones, sl2, rescale_thr, A, NoMask{});
-        }
       }
+      wait_and_barrier<0>();
+      if constexpr (kOn) last_step(two_left ? st1 : st0);
     };
     if (wave_on)
       tiles(std::true_type{});
