@@ -128,8 +128,12 @@ __device__ __forceinline__ void dkdv_step(const LDS char* base, const Lanes& L, 
   const bool masked_tile = kMask && (diag || qvalid < kTileRows);
   const int qlo = diag ? key : 0;
   const uint32_t qspan = (uint32_t)max(qvalid - qlo, 0);
+  // On the diagonal tile the queries of half hh all precede this wave's keys
+  // when 32 hh + 31 < 16 w: the half weighs nothing and is skipped (uniform).
+  const int wu = __builtin_amdgcn_readfirstlane(L.wid);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
+    if (kMask && diag && 2 * hh + 1 < wu) continue;
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -336,13 +340,17 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dkdv_kernel(const uint16_t* 
 // One key tile of a dQ item: S^T = K Q^T, dP^T = V dO^T (keys as rows: lane
 // (g, lq) holds keys 16 b + 4 g + r of the wave's query lq), dS^T, then
 // dQ^T += K^T dS^T.  nlse: -(log-sum-exp) log2(e) of the lane's query; dd: its
-// D.  kDiag: keys after the lane's query row qr are masked.
-template <bool kDiag>
+// D.  kDiagW >= 0: the diagonal tile as wave kDiagW sees it -- key blocks below
+// the wave's rows are visible whole, block kDiagW up to the lane's own row, and
+// the blocks above are neither formed nor weighed (their dS is exactly 0).
+template <int kDiagW>
 __device__ __forceinline__ void dq_step(const LDS char* base, const Lanes& L, const bf16x8 (&qf)[2],
                                         const bf16x8 (&of)[2], float sl2, float nlse, float dd, f32x4 (&dq)[4]) {
+  constexpr int kNB = kDiagW < 0 ? 4 : kDiagW + 1;  // key blocks formed
   f32x4 s[4], dp[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
+    if (b >= kNB) break;
     const bf16x8 k0 = lds_b128(base, L.kofs[0] + 2048 * b);
     const bf16x8 k1 = lds_b128(base, L.kofs[1] + 2048 * b);
     s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -354,16 +362,23 @@ __device__ __forceinline__ void dq_step(const LDS char* base, const Lanes& L, co
   }
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
+    if (2 * hh >= kNB) break;
+    const bool two = 2 * hh + 1 < kNB;  // the half's second block is formed
     uint32_t dw[4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int b = 2 * hh + half;
+      if (b >= kNB) {
+        dw[2 * half] = 0u;
+        dw[2 * half + 1] = 0u;
+        continue;
+      }
       float ds[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], sl2, nlse));
         ds[r] = p * (dp[b][r] - dd);
-        if (kDiag && 16 * b + 4 * L.g + r > L.qr) ds[r] = 0.f;
+        if (b == kDiagW && 4 * L.g + r > L.lq) ds[r] = 0.f;
       }
       dw[2 * half] = pack_bf16x2(ds[0], ds[1]);
       dw[2 * half + 1] = pack_bf16x2(ds[2], ds[3]);
@@ -371,9 +386,10 @@ __device__ __forceinline__ void dq_step(const LDS char* base, const Lanes& L, co
     const bf16x8 db = __builtin_bit_cast(bf16x8, uint4{dw[0], dw[1], dw[2], dw[3]});
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      // K^T fragments (the K half of the stage) for keys 32 hh .. 32 hh + 31.
+      // K^T fragments (the K half of the stage) for keys 32 hh .. 32 hh + 31; an
+      // unformed second block is taken as 0.
       const bf16x4 lo = lds_tr16(base, L.vofs[d] - kTileBytes + 4096 * hh);
-      const bf16x4 hi = lds_tr16(base, L.vofs[d] - kTileBytes + 4096 * hh + 2048);
+      const bf16x4 hi = two ? lds_tr16(base, L.vofs[d] - kTileBytes + 4096 * hh + 2048) : bf16x4{};
       dq[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), db,
                                                       dq[d], 0, 0, 0);
     }
@@ -455,27 +471,35 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(const uint16_t* __
     // q-tile) computes nothing: it issues its share of the copies and meets the
     // barriers, in a second copy of the loop.
     const int khi = qt + 1;
+    // The diagonal tile, specialised for each wave; it ends an item once, so its
+    // stage is a run-time choice.
+    auto diag_step = [&](const LDS char* base) {
+      switch (__builtin_amdgcn_readfirstlane(L.wid)) {
+        case 0: dq_step<0>(base, L, qf, of, sl2, nlse, dd, dq); break;
+        case 1: dq_step<1>(base, L, qf, of, sl2, nlse, dd, dq); break;
+        case 2: dq_step<2>(base, L, qf, of, sl2, nlse, dd, dq); break;
+        default: dq_step<3>(base, L, qf, of, sl2, nlse, dd, dq); break;
+      }
+    };
     auto tiles = [&](auto compute) {
       constexpr bool kOn = decltype(compute)::value;
       int j = 0;
       for (; j + 2 < khi; j += 2) {
         wait_and_barrier<0>();
         issue_tile(kStageBytes, j + 1);
-        if constexpr (kOn) dq_step<false>(st0, L, qf, of, sl2, nlse, dd, dq);
+        if constexpr (kOn) dq_step<-1>(st0, L, qf, of, sl2, nlse, dd, dq);
         wait_and_barrier<0>();
         issue_tile(0, j + 2);
-        if constexpr (kOn) dq_step<false>(st1, L, qf, of, sl2, nlse, dd, dq);
+        if constexpr (kOn) dq_step<-1>(st1, L, qf, of, sl2, nlse, dd, dq);
       }
-      if (j + 1 < khi) {
+      const bool two_left = j + 1 < khi;
+      if (two_left) {
         wait_and_barrier<0>();
         issue_tile(kStageBytes, j + 1);
-        if constexpr (kOn) dq_step<false>(st0, L, qf, of, sl2, nlse, dd, dq);
-        wait_and_barrier<0>();
-        if constexpr (kOn) dq_step<true>(st1, L, qf, of, sl2, nlse, dd, dq);
-      } else {
-        wait_and_barrier<0>();
-        if constexpr (kOn) dq_step<true>(st0, L, qf, of, sl2, nlse, dd, dq);
+        if constexpr (kOn) dq_step<-1>(st0, L, qf, of, sl2, nlse, dd, dq);
       }
+      wait_and_barrier<0>();
+      if constexpr (kOn) diag_step(two_left ? st1 : st0);
     };
     if (__builtin_amdgcn_readfirstlane(16 * L.wid < len - q0))
       tiles(std::true_type{});
