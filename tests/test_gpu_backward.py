@@ -83,6 +83,9 @@ CASES = {
     "sixteen_heads": dict(lengths=[33, 190], n_heads=16),
     "scaled_values_x2": dict(lengths=[300, 17], value_scale=2.0),
     "300_users": dict(lengths=list(np.random.default_rng(5).integers(0, 150, 300))),
+    # Users whose rows end at each of the 64 positions of their diagonal tile, in
+    # one-tile and two-tile users (every wave's diagonal step, dQ and dK/dV).
+    "diag_every_residue": dict(lengths=list(range(1, 129)), n_heads=1),
 }
 
 

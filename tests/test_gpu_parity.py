@@ -34,6 +34,12 @@ SMALL_CASES = {
     "split_three_heads": dict(lengths=[700, 12, 300], n_heads=3),
     "split_sixteen_heads": dict(lengths=[1000, 1000], n_heads=16),
     "split_scaled_values_x4": dict(lengths=[600, 33], value_scale=4.0),
+    # The diagonal tile of every wave with the user's rows ending at each of the
+    # 64 positions in the tile: one-tile users of 1..64 rows, two-tile users of
+    # 65..128 rows (one head keeps the oracle fast; 128 users take the shared
+    # prologue path).
+    "diag_every_residue": dict(lengths=list(range(1, 129)), n_heads=1),
+    "diag_every_residue_one_wave_prologue": dict(lengths=list(range(1, 65)), n_heads=2),
 }
 
 
