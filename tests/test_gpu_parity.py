@@ -125,3 +125,28 @@ def test_balanced_one_round_sampled_rows(gpu, name):
     rows = sample_rows(w, np.random.default_rng(21))
     ref = oracle.varlen_causal_attention_rows(qkv64(w), w.cu_seqlens, rows, w.n_heads, w.head_dim, w.scale)
     assert_close(out[rows], ref, f"{name} ({rows.size} sampled rows)")
+
+
+def test_max_length_users_past_2gib_sampled_rows(gpu):
+    """Three users of the maximum length (262144 rows = 4096 q-tiles, the
+    largest max_seqlen accepted) and two short ones, 8 heads: 2.4 GB of qkv, so
+    the third user's rows lie past 2 GiB of byte offset.  Sampled rows (each
+    user's first rows and tile edges, a few deep rows, the short users whole)
+    against the oracle evaluated one row at a time."""
+    L = 262144
+    lengths = [L, 5, L, 1, L]
+    w = workloads.make_from_lengths(lengths, seed=41, max_seqlen=L)
+    say(f"[case] max-length users T={w.total_tokens} qkv {w.total_tokens * 3072 / 2**30:.2f} GiB")
+    out = run_fwd(w)
+    cu = [int(c) for c in w.cu_seqlens]
+    rows = []
+    for u, n in enumerate(lengths):
+        s = cu[u]
+        if n <= 64:
+            rows.extend(range(s, s + n))
+        else:
+            rows.extend(s + r for r in (0, 1, 2, 63, 64, 65, 127, 128, 4095, 4096, 65537, n - 1))
+    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    ref = oracle.varlen_causal_attention_rows(w.qkv_bf16.float().numpy(), w.cu_seqlens, rows, w.n_heads,
+                                              w.head_dim, w.scale)
+    assert_close(out[rows], ref, f"max-length users ({rows.size} sampled rows)")
