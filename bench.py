@@ -30,10 +30,10 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 CSRC = os.path.join(ROOT, "varlen_causal_attention_amd", "csrc")
 # The device sources each measured path runs (the profiles record their hash).
 KERNEL_SOURCES = {
-    "fwd": ("vlca_device.h", "vlca_kernels.hip"),
-    "bwd": ("vlca_device.h", "vlca_kernels.hip", "vlca_backward.hip"),
-    "masked": ("vlca_device.h", "vlca_kernels.hip", "vlca_masked.hip"),
-    "layer": ("vlca_device.h", "vlca_kernels.hip", "vlca_proj.hip"),
+    "fwd": ("vlca_device.h", "vlca_order.h", "vlca_kernels.hip"),
+    "bwd": ("vlca_device.h", "vlca_order.h", "vlca_kernels.hip", "vlca_backward.hip"),
+    "masked": ("vlca_device.h", "vlca_order.h", "vlca_kernels.hip", "vlca_masked.hip"),
+    "layer": ("vlca_device.h", "vlca_order.h", "vlca_kernels.hip", "vlca_proj.hip"),
 }
 ATTN_KERNEL = "attention_kernel"  # <true, true, false>: single-kernel plan; <false, ...>: over a worklist
 PROFILE_PREFIX = {"fwd": "attention_kernel", "bwd": "backward", "masked": "masked_attention_kernel",

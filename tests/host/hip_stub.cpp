@@ -243,7 +243,15 @@ hipError_t launch_masked_attention(const void*, const int4* items, const int32_t
   return hipSuccess;
 }
 
-int masked_blocks_per_cu() { return g.blocks_per_cu; }
+hipError_t launch_masked_attention_fused(const void*, const int32_t*, int num_users, int max_tiles, int n_heads, float,
+                                         const int32_t*, const int32_t*, int, int, int, void*, int grid,
+                                         int layer_log2, hipStream_t stream) {
+  g.launches.push_back({'M', nullptr, 0, num_users, max_tiles, n_heads, grid, layer_log2,
+                        {0, 0, 0, nullptr, nullptr}, stream});
+  return hipSuccess;
+}
+
+int masked_blocks_per_cu(bool) { return g.blocks_per_cu; }
 
 hipError_t launch_ln_qkv(const void*, const void*, const void*, float, const void*, const void*, int T, int N, void*,
                          int, hipStream_t stream) {

@@ -298,15 +298,25 @@ static void test_masked_entry_point() {
   vlca_mask causal{nullptr, nullptr, 1, -1, 0};
   CHECK(fm(&causal, 60, 452) == VLCA_OK && fm(nullptr, 60, 452) == VLCA_OK);
   CHECK(g.launches.size() == 2 && g.launches[0].kind == 'f' && g.launches[1].kind == 'f');
-  // A window, contexts and targets: the scheduler, then the masked kernel over its worklist.
+  // A window, contexts and targets on a small batch (the causal forward's
+  // single-kernel condition): the masked kernel alone, locating its own items.
   g.launches.clear();
   vlca_mask hstu{ctx, tgt, 4, 256, 0};
   CHECK(fm(&hstu, 60, 452) == VLCA_OK);
+  CHECK(g.launches.size() == 1 && g.launches[0].kind == 'M');
+  CHECK(g.launches[0].num_users == 60 && g.launches[0].max_tiles == 8 && g.launches[0].grid == 1024);
+  CHECK(g.launches[0].layer_log2 == -1);  // 60 x 8 units per head exceed one round of 128 slots
+  CHECK(fm(&hstu, 4, 1024) == VLCA_OK && g.launches.back().kind == 'M' && g.launches.back().grid == 512);
+  CHECK(g.launches.back().layer_log2 == 5);  // 4 x 16 units per head fit one round: layers of 32 slots
+  // Larger batches: the scheduler, then the masked kernel over its worklist.
+  g.launches.clear();
+  CHECK(fm(&hstu, 300, 452) == VLCA_OK);
   CHECK(g.launches.size() == 2 && g.launches[0].kind == 's' && g.launches[1].kind == 'm');
   CHECK(g.launches[1].items == g.launches[0].items && g.launches[1].num_users == 4);
   CHECK(g.launches[1].max_tiles == 256 && g.launches[1].layer_log2 == 0 && g.launches[1].grid == 1024);
   vlca_mask bidir{nullptr, nullptr, 1, -1, -1};
-  CHECK(fm(&bidir, 60, 452) == VLCA_OK && g.launches.back().kind == 'm' && g.launches.back().layer_log2 == -1);
+  CHECK(fm(&bidir, 300, 452) == VLCA_OK && g.launches.back().kind == 'm' && g.launches.back().layer_log2 == -1);
+  CHECK(fm(&bidir, 60, 452) == VLCA_OK && g.launches.back().kind == 'M');
   CHECK(g.frees == 0 && g.syncs == 0);
 }
 

@@ -330,17 +330,37 @@ int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, in
   if (num_users == 0 || max_seqlen == 0) return VLCA_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return VLCA_ERR_HIP;
+  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
+  // Small batches (the causal forward's condition): one kernel that locates its
+  // own items.  Each item computes the same thing on either plan, so the choice
+  // changes no bits.
+  {
+    const int64_t pairs = item_pairs(num_users, max_seqlen, n_heads);
+    int64_t g = static_cast<int64_t>(cu_count(dev)) * vlca::masked_blocks_per_cu(true);
+    g = std::min<int64_t>(g, vlca::kMaxGrid);
+    g -= g % 8;
+    g = std::max<int64_t>(std::min<int64_t>(g, pairs), 1);
+    const int grid = static_cast<int>(g);
+    if (vlca::fused_fits(num_users, max_tiles, n_heads, grid)) {
+      const int layer_log2 = snake_layer_log2(dev, grid, n_heads, static_cast<int64_t>(num_users) * max_tiles);
+      if (vlca::launch_masked_attention_fused(qkv, cu_seqlens, num_users, max_tiles, n_heads, scale * kLog2e,
+                                              mask->num_contexts, mask->num_targets, mask->target_group_size,
+                                              mask->window_left, mask->window_right, out, grid, layer_log2,
+                                              stream) != hipSuccess)
+        return VLCA_ERR_HIP;
+      return VLCA_OK;
+    }
+  }
   const int64_t need = required_capacity(num_users, max_seqlen);
   StreamState st;
   rc = get_workspace(dev, stream, need, &st);
   if (rc != VLCA_OK) return rc;
-  const int max_tiles = static_cast<int>(max_tiles_of(max_seqlen));
   int32_t* count = workspace_count(&st);
   int32_t* queue = count + vlca::kQueueStride;
   if (vlca::launch_schedule(cu_seqlens, num_users, max_tiles, st.items, count, queue,
                             vlca::SplitArgs{0, 0, 0, nullptr, nullptr}, stream) != hipSuccess)
     return VLCA_ERR_HIP;
-  int64_t g = static_cast<int64_t>(cu_count(dev)) * vlca::masked_blocks_per_cu();
+  int64_t g = static_cast<int64_t>(cu_count(dev)) * vlca::masked_blocks_per_cu(false);
   g = std::min<int64_t>(g, vlca::kMaxGrid);
   g -= g % 8;
   g = std::max<int64_t>(std::min<int64_t>(g, need * n_heads), 1);

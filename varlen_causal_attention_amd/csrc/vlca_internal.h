@@ -103,7 +103,13 @@ hipError_t launch_masked_attention(const void* qkv, const int4* items, const int
                                    int n_heads, float scale_log2e, const int32_t* num_contexts,
                                    const int32_t* num_targets, int group, int window_left, int window_right,
                                    void* out, int grid, hipStream_t stream);
-int masked_blocks_per_cu();
+// The same forward as one kernel for batches where fused_fits() holds: every
+// workgroup locates its own items from cu_seqlens (no worklist, no counters).
+hipError_t launch_masked_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
+                                         int n_heads, float scale_log2e, const int32_t* num_contexts,
+                                         const int32_t* num_targets, int group, int window_left, int window_right,
+                                         void* out, int grid, int layer_log2, hipStream_t stream);
+int masked_blocks_per_cu(bool fused);
 
 // The attention's neighbours in the packed layer (vlca_proj.hip), d_in = 512,
 // N a multiple of 128 (at most kMaxProjOut): qkv = LayerNorm(x) W_qkv^T + b_qkv,

@@ -33,6 +33,7 @@
 
 #include "vlca_device.h"
 #include "vlca_internal.h"
+#include "vlca_order.h"
 
 namespace vlca {
 namespace {
@@ -68,10 +69,17 @@ __device__ __forceinline__ void as_span(int lo, int hi, int& start, int& span) {
   span = empty ? 0 : hi - lo;
 }
 
+// kFused = false: the items of the scheduler's worklist (items, count), claimed
+// per head after two rounds of the snake.  kFused = true (single-kernel plan,
+// the causal forward's condition): every workgroup locates its own items of the
+// same list from cu_seqlens (own_units, vlca_order.h) and takes them in the
+// fixed snake (layered when layer_log2 >= 0).
+template <bool kFused>
 __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
     const uint16_t* __restrict__ qkv, const int4* __restrict__ items, const int32_t* __restrict__ count,
-    int32_t* __restrict__ queue, int n_heads, float sl2, const int32_t* __restrict__ num_contexts,
-    const int32_t* __restrict__ num_targets, int group, int wl, int wr, uint16_t* __restrict__ out) {
+    int32_t* __restrict__ queue, const int32_t* __restrict__ cu, int U, int max_tiles, int layer_log2, int n_heads,
+    float sl2, const int32_t* __restrict__ num_contexts, const int32_t* __restrict__ num_targets, int group, int wl,
+    int wr, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char ring_lds[2 * kStageBytes];
   LDS char* const st0 = (LDS char*)ring_lds;
   LDS char* const st1 = st0 + kStageBytes;
@@ -86,6 +94,22 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(st0 + 2048 * L.wid));
   const bool causal = wr == 0;
 
+  // The workgroup's own items (single-kernel plan): descriptors (q_tile,
+  // row_start, length, head | user << 16), negative past its last round; until
+  // they are known the workgroup runs at the highest wave priority, so that
+  // co-resident workgroups already inside items do not starve the ordering.
+  __shared__ i32x4 s_desc[kFused ? kWaves * kDescRounds : 1];
+  int desc_base = 0;
+  if constexpr (kFused) {
+    __builtin_amdgcn_s_setprio(3);
+    const Snake sn(n_heads, layer_log2);
+    auto work_of = [&](int round, int& item, int& h) { sn.unit(round, item, h); };
+    if (!own_units<true>(cu, U, max_tiles, SplitArgs{0, 0, 0, nullptr, nullptr}, L, st0, (LDS i32x4*)s_desc,
+                         work_of, desc_base))
+      return;
+    __builtin_amdgcn_s_setprio(0);
+  }
+
   // Work units: with the grid a multiple of H (and H <= kQueues), head g % H,
   // units counted per head; else units over (item, head) pairs.  The first two
   // rounds follow the snake over the list; later items are claimed from counter
@@ -98,24 +122,42 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
   int32_t* const qctr = queue + (per_head ? head0 : 0) * kQueueStride;
   const int nslots = per_head ? gridDim.x / n_heads : gridDim.x;
   const int wfirst = per_head ? blockIdx.x / n_heads : blockIdx.x;
-  const int nitems = *count;
+  const int nitems = kFused ? 0 : *count;
   __shared__ int s_next;
   for (int round = 0;; ++round) {
-    const int w = round == 0 ? wfirst : round == 1 ? 2 * nslots - 1 - wfirst : __builtin_amdgcn_readfirstlane(s_next);
-    int item, h;
-    if (per_head) {
-      item = w;
-      h = head0;
-    } else {
-      item = w / n_heads;
-      h = w - item * n_heads;
-    }
-    if (item >= nitems) break;
+    int h, u, qt, start, len;
     int claimed = 0;
-    if (round >= 1 && threadIdx.x == 0)
-      claimed = 2 * nslots + __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int4 it = items[item];
-    const int u = it.x, qt = it.y & 0xffff, start = it.z, len = it.w;
+    if constexpr (kFused) {
+      if (round >= kDescRounds) break;
+      const i32x4 d = s_desc[desc_base + round];
+      const int w0 = __builtin_amdgcn_readfirstlane(d[0]);
+      if (w0 < 0) break;
+      qt = w0 & 0xffff;
+      start = __builtin_amdgcn_readfirstlane(d[1]);
+      len = __builtin_amdgcn_readfirstlane(d[2]);
+      const int w3 = __builtin_amdgcn_readfirstlane(d[3]);
+      h = w3 & 0xffff;
+      u = w3 >> 16;
+    } else {
+      const int w =
+          round == 0 ? wfirst : round == 1 ? 2 * nslots - 1 - wfirst : __builtin_amdgcn_readfirstlane(s_next);
+      int item;
+      if (per_head) {
+        item = w;
+        h = head0;
+      } else {
+        item = w / n_heads;
+        h = w - item * n_heads;
+      }
+      if (item >= nitems) break;
+      if (round >= 1 && threadIdx.x == 0)
+        claimed = 2 * nslots + __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int4 it = items[item];
+      u = it.x;
+      qt = it.y & 0xffff;
+      start = it.z;
+      len = it.w;
+    }
     const int q0 = qt * kTileRows;
     const int lim = len - 1 - q0;
     // The user's mask geometry (clamped to its length).
@@ -265,7 +307,7 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
       tiles(std::true_type{});
     else
       tiles(std::false_type{});
-    if (round >= 1 && threadIdx.x == 0) s_next = claimed;
+    if (!kFused && round >= 1 && threadIdx.x == 0) s_next = claimed;
     wait_and_barrier<0>();  // every wave is done with the ring; s_next is visible
     store_rows(st0 + 2048 * L.wid, A.o, 1.0f / A.l[0],
                out + ((int64_t)start + q0 + 16 * L.wid) * ldo + h * kHeadDim, ldo, len - q0 - 16 * L.wid);
@@ -278,17 +320,29 @@ hipError_t launch_masked_attention(const void* qkv, const int4* items, const int
                                    int n_heads, float scale_log2e, const int32_t* num_contexts,
                                    const int32_t* num_targets, int group, int window_left, int window_right,
                                    void* out, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(masked_attention_kernel, dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const uint16_t*>(qkv), items, count, queue, n_heads, scale_log2e, num_contexts,
-                     num_targets, group, window_left, window_right, static_cast<uint16_t*>(out));
+  hipLaunchKernelGGL(masked_attention_kernel<false>, dim3(grid), dim3(kAttnThreads), 0, stream,
+                     static_cast<const uint16_t*>(qkv), items, count, queue, nullptr, 0, 0, -1, n_heads, scale_log2e,
+                     num_contexts, num_targets, group, window_left, window_right, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
-int masked_blocks_per_cu() {
+hipError_t launch_masked_attention_fused(const void* qkv, const int32_t* cu_seqlens, int num_users, int max_tiles,
+                                         int n_heads, float scale_log2e, const int32_t* num_contexts,
+                                         const int32_t* num_targets, int group, int window_left, int window_right,
+                                         void* out, int grid, int layer_log2, hipStream_t stream) {
+  hipLaunchKernelGGL(masked_attention_kernel<true>, dim3(grid), dim3(kAttnThreads), 0, stream,
+                     static_cast<const uint16_t*>(qkv), nullptr, nullptr, nullptr, cu_seqlens, num_users, max_tiles,
+                     layer_log2, n_heads, scale_log2e, num_contexts, num_targets, group, window_left, window_right,
+                     static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+int masked_blocks_per_cu(bool fused) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, masked_attention_kernel, kAttnThreads, 0) != hipSuccess ||
-      n < 1)
-    n = 1;
+  const hipError_t e =
+      fused ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, masked_attention_kernel<true>, kAttnThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, masked_attention_kernel<false>, kAttnThreads, 0);
+  if (e != hipSuccess || n < 1) n = 1;
   return n;
 }
 
