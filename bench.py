@@ -580,8 +580,9 @@ def visible_pairs(lengths, c, g, group, window) -> int:
 
 
 def run_masked(args, w, dev):
-    """One step = one varlen_causal_attn_fwd_masked call (scheduler + masked kernel)
-    with MASK_RECIPE's per-user counts and window."""
+    """One step = one varlen_causal_attn_fwd_masked call with MASK_RECIPE's per-user
+    counts and window: the masked kernel alone on batches of the single-kernel
+    plan, the scheduler and the masked kernel on larger ones."""
     import torch
 
     import varlen_causal_attention_amd as vlca
@@ -624,7 +625,8 @@ def run_masked(args, w, dev):
         "tflops": flops / (ms_step * 1e-3) / 1e12,
         "pct_bf16_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": roofline(flops, nbytes, ms_step * 1e-3, measured_traffic(w.name, "masked"),
-                             "varlen_causal_attn_fwd_masked (scheduler + masked_attention_kernel)"),
+                             "varlen_causal_attn_fwd_masked (masked_attention_kernel, after the scheduler on "
+                             "batches past the single-kernel plan)"),
     }), flush=True)
 
 
