@@ -118,3 +118,24 @@ def test_bad_masks_raise(gpu):
         with pytest.raises(vlca.VlcaError) as e:
             vlca.fwd_masked(qkv, cu, w.max_seqlen, **kw)
         assert e.value.code == -13
+
+
+def test_masked_single_kernel_shared_ordering(gpu):
+    """200 users (more than 64: the single-kernel plan orders them one user per
+    thread and shares the descriptors), zero-length users among them, with
+    contexts, candidate groups and a window, against the oracle; the scheduler
+    plan (forced by a large max_seqlen) gives the same bits."""
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(0, 150, 200)]
+    w = workloads.make_from_lengths(lengths, seed=77)
+    c = [int(x) for x in rng.integers(0, 20, 200)]
+    g = [int(x) for x in rng.integers(0, 30, 200)]
+    assert vlca.single_kernel(w.num_users, w.max_seqlen, w.n_heads)
+    assert not vlca.single_kernel(w.num_users, 65536, w.n_heads)
+    say(f"[case] masked, 200 users T={w.total_tokens}")
+    out = _run(w, c=c, g=g, group=4, window=(48, 0))
+    ref = oracle.varlen_attention_masked(qkv64(w), w.cu_seqlens, 8, 64, w.scale, num_contexts=c, num_targets=g,
+                                         group=4, window=(48, 0))
+    assert_close(out, ref, "masked, 200 users")
+    out2 = _run(w, c=c, g=g, group=4, window=(48, 0), max_seqlen=65536)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
