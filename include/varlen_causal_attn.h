@@ -167,9 +167,11 @@ typedef struct vlca_mask {
  * varlen_causal_attn_fwd; mask (host pointer, read during the call) as above.
  * mask NULL, or the plain causal mask (no contexts, no targets, window (-1, 0)),
  * runs varlen_causal_attn_fwd itself (same bits).  Other masks run a separate
- * kernel over the stream's worklist (allocated or grown on first need, never
- * freed), whose result equals the definition within rounding.  Errors as for
- * varlen_causal_attn_fwd, plus VLCA_ERR_MASK.
+ * kernel whose result equals the definition within rounding: on the batches
+ * where varlen_causal_attn_fwd runs one kernel (varlen_causal_attn_single_kernel)
+ * it alone, locating its own items (no worklist, no allocation); otherwise over
+ * the stream's worklist (allocated or grown on first need, never freed).  Both
+ * give the same bits.  Errors as for varlen_causal_attn_fwd, plus VLCA_ERR_MASK.
  */
 int varlen_causal_attn_fwd_masked(const void* qkv, const int32_t* cu_seqlens, int num_users,
                                   int max_seqlen, int n_heads, int head_dim, float scale,
