@@ -490,10 +490,10 @@ __device__ __forceinline__ void attention_body(const uint16_t* __restrict__ qkv,
 
   // kFused: the workgroup's unit descriptors (q_tile | kind << 16, row_start,
   // length, head | split rank of part 0 << 16), negative past its last round;
-  // shared by the waves, or one copy per wave when each wave orders the users.
+  // shared by the waves.
   // kind: 0 the whole item, 1 / 2 its first / second key-range part.
-  __shared__ i32x4 s_desc[kFused ? kWaves * kDescRounds : 1];
-  int desc_base = 0;  // this wave's descriptors: s_desc[desc_base + round]
+  __shared__ i32x4 s_desc[kFused ? kDescRounds : 1];
+  int desc_base = 0;  // the descriptors: s_desc[desc_base + round]
   __shared__ int s_arrived;
   int nitems = 0, qt_max = 0;
   if constexpr (kFused) {

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kAttnThreads, 4) void masked_attention_kernel(
   // row_start, length, head | user << 16), negative past its last round; until
   // they are known the workgroup runs at the highest wave priority, so that
   // co-resident workgroups already inside items do not starve the ordering.
-  __shared__ i32x4 s_desc[kFused ? kWaves * kDescRounds : 1];
+  __shared__ i32x4 s_desc[kFused ? kDescRounds : 1];
   int desc_base = 0;
   if constexpr (kFused) {
     __builtin_amdgcn_s_setprio(3);

@@ -146,10 +146,10 @@ struct Snake {
 // (q_tile | kind << 16, row_start, length, head | split rank of part 0 << 16)
 // -- with kUser (no splitting) head | user << 16 -- negative past its last
 // round; kind 0 is a whole item, 1 / 2 its first / second key-range part.  The
-// descriptors are shared by the waves (desc_base 0) or, when each wave orders
-// the users itself, one copy per wave at desc_base.  `scratch` (at least
-// kWaves * kClasses ints of LDS) is free again on return.  Returns false, for
-// every thread of the workgroup, when the workgroup has no unit.
+// descriptors (kDescRounds of them) are shared by the waves; desc_base is 0.
+// `scratch` (at least kWaves * kClasses ints of LDS) is free again on return.
+// Returns false, for every thread of the workgroup, when the workgroup has no
+// unit.
 template <bool kUser, typename WorkOf>
 __device__ __forceinline__ bool own_units(const int32_t* __restrict__ cu, int U, int max_tiles, const SplitArgs& sp,
                                           const Lanes& L, LDS char* scratch, LDS i32x4* s_desc,
@@ -167,10 +167,18 @@ __device__ __forceinline__ bool own_units(const int32_t* __restrict__ cu, int U,
   const int lane = L.lane;
   const int nusers = max_tiles > 0 ? U : 0;
   const int total = nusers > 0 ? cu[nusers] : 0;
-  // At most 64 users: every wave orders them by itself (a user per lane), with
-  // no LDS exchange and no barrier, and keeps its own copy of the descriptors.
-  // Otherwise one user per thread, per-wave class sums through LDS.
+  // At most 64 users: one wave of the workgroup orders them (a user per lane)
+  // and writes the shared descriptors; the other waves wait at the one barrier.
+  // The ordering wave is 0..3 by the workgroup's layer on its CU (workgroups g,
+  // g + 256, ... share a CU on a 256-CU device), so the co-resident workgroups'
+  // ordering waves do not all share one SIMD.  Otherwise one user per thread,
+  // per-wave class sums through LDS.
   const bool one_wave = nusers <= 64;
+  if (one_wave && __builtin_amdgcn_readfirstlane(L.wid) != ((blockIdx.x >> 8) & (kWaves - 1))) {
+    lds_barrier();
+    desc_base = 0;
+    return __builtin_amdgcn_readfirstlane(s_desc[0][0]) >= 0;
+  }
   const int me = one_wave ? lane : threadIdx.x;  // this thread's user
   Seg sg{0, 0, 0};
   if (me < nusers) sg = segment_of(cu, cu, false, me, total, max_tiles);
@@ -232,7 +240,7 @@ __device__ __forceinline__ bool own_units(const int32_t* __restrict__ cu, int U,
   {  // a workgroup past the last item (the grid may exceed the work) leaves now
     int item0, h0;
     work_of(0, item0, h0);
-    if (item0 >= n) return false;  // uniform across the workgroup
+    if (item0 >= n && !one_wave) return false;  // uniform (one wave: the descriptors say so)
   }
   // The user's first unit, and the split rank of its first split part (two per
   // split item of the users before it).
@@ -241,7 +249,7 @@ __device__ __forceinline__ bool own_units(const int32_t* __restrict__ cu, int U,
   // Units of later rounds lie further down the list, so the first round past
   // the end closes the descriptors.  (The list without split items has its own
   // copy of the loop: it is on every batch's critical path.)
-  LDS i32x4* const desc = s_desc + (one_wave ? L.wid * kDescRounds : 0);
+  LDS i32x4* const desc = s_desc;
   const bool writer = one_wave ? lane == 0 : threadIdx.x == 0;
   auto fill = [&](auto with_split) {
     for (int r = 0; r < kDescRounds; ++r) {
@@ -269,15 +277,9 @@ __device__ __forceinline__ bool own_units(const int32_t* __restrict__ cu, int U,
     fill(std::true_type{});
   else
     fill(std::false_type{});
-  if (one_wave) {
-    // The descriptors came from lanes of this wave: wait for the writes.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
-  } else {
-    lds_barrier();  // descriptors visible; the ring is free again
-  }
-  desc_base = one_wave ? L.wid * kDescRounds : 0;
-  return true;
+  lds_barrier();  // descriptors visible to every wave; the ring is free again
+  desc_base = 0;
+  return !one_wave || __builtin_amdgcn_readfirstlane(s_desc[0][0]) >= 0;
 }
 
 }  // namespace
